@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Throughput of the routed MoE layer on one MI355X.
+
+Default workload: bf16 prefill chunk, hidden 2048, 128 routed experts
+(gate/up 2048x512, down 512x2048) top-8 plus one shared expert, T = 256
+tokens.  A step is one pass of the whole layer (route, permute, grouped
+gate/up + SwiGLU, grouped down, combine) over one batch of fresh synthetic
+tokens, inputs already resident in HBM.  Weight sets rotate every step so the
+256 MB MALL cannot serve repeated weight reads.
+
+Prints ONE JSON line: tokens/s per layer, the gate/up kernel against the HBM
+roofline, the int8 T = 8 decode layer as a secondary figure, and the CPU
+oracle timed on a bounded sample as a reported baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+METRIC = "routed tokens/s per MoE layer (T=256 prefill, T=8 decode); % MFMA / HBM peak"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_bytes(spec, n, k):
+    """Bytes of one group's [n][k] weight matrix in its storage format (with scales)."""
+    if spec.wt == "f32":
+        return n * k * 4
+    if spec.wt == "bf16":
+        return n * k * 2
+    if spec.wt == "i8":
+        return n * k + n * 4
+    return n * k // 2 + 2 * (n * k // 32) * 2
+
+
+def act_bytes(spec):
+    return 4 if spec.act == "f32" else 2
+
+
+def gu_algorithmic_bytes(spec, T, U):
+    """Gate/up launch: weights of the U touched groups, tokens read once, h written once."""
+    R = T * (spec.top_k + spec.n_shared)
+    xb = T * spec.hidden * (1 if spec.wt == "i8" else act_bytes(spec)) + (T * 4 if spec.wt == "i8" else 0)
+    hb = R * spec.inter * (4 if spec.wt in ("f32", "i8") else 2)
+    return U * weight_bytes(spec, 2 * spec.inter, spec.hidden) + xb + hb
+
+
+def down_algorithmic_bytes(spec, T, U):
+    R = T * (spec.top_k + spec.n_shared)
+    ib = R * spec.inter * (1 if spec.wt == "i8" else (4 if spec.wt == "f32" else 2))
+    yb = R * spec.hidden * (4 if spec.wt in ("f32", "i8") else 2)
+    return U * weight_bytes(spec, spec.hidden, spec.inter) + ib + yb
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, launch_algo_bytes):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest(rec.get("sources", [])):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Runner:
+    """Device-resident inputs of one workload and its MoeLayer."""
+
+    def __init__(self, name, T, rotations, n_batches):
+        import torch
+        from gen import synth
+        from mixture_experts_expert_moe_amd import moe
+        from tests import gpu_harness as gh
+
+        self.torch, self.moe = torch, moe
+        self.name, self.T = name, T
+        wid = synth.workload_id(name)
+        self.spec = spec = synth.workload(name).spec
+        t0 = time.time()
+        self.wsets = []
+        for r in range(rotations):
+            host = synth.layer_weights(spec, wid, 0, r)
+            self.wsets.append(gh.dev_weights(host))
+            del host
+        self.x = [gh.to_dev(synth.tokens(spec, wid, T, stream=1000 + i)) for i in range(n_batches)]
+        log("[bench] %s: %d weight sets + %d token batches generated and uploaded in %.1f s"
+            % (name, rotations, n_batches, time.time() - t0))
+        self.desc = gh.desc_for(spec, T)
+        self.layer = moe.MoeLayer(self.desc, self.wsets[0])
+        self.structs = [(moe.weights_struct(w["w_gu"], w["w_gu_scale"], w["w_gu_min"]),
+                         moe.weights_struct(w["w_down"], w["w_down_scale"], w["w_down_min"])) for w in self.wsets]
+        odt = torch.float32 if spec.out == "f32" else torch.bfloat16
+        self.out = torch.empty((T, spec.hidden), dtype=odt, device="cuda")
+
+    def step(self, i, ev=None):
+        """One layer: route, permute, gate/up, down, combine.  ev: optional list of
+        6 events recorded around the launches (same stream as the kernels)."""
+        moe, d, b, T = self.moe, self.desc, self.layer.bufs, self.T
+        w = self.wsets[i % len(self.wsets)]
+        gu, dn = self.structs[i % len(self.wsets)]
+        x = self.x[i % len(self.x)]
+        if ev:
+            ev[0].record()
+        moe.moe_route_topk(d, T, x, w["w_router"], w.get("bias"), b)
+        if ev:
+            ev[1].record()
+        moe.moe_permute(d, T, x, b)
+        if ev:
+            ev[2].record()
+        moe.moe_grouped_gemm_gu(d, T, x, gu, b)
+        if ev:
+            ev[3].record()
+        moe.moe_grouped_gemm_down(d, T, dn, b)
+        if ev:
+            ev[4].record()
+        moe.moe_combine(d, T, None, self.out, b)
+        if ev:
+            ev[5].record()
+
+    def touched_groups(self):
+        offs = self.layer.tensors["expert_offsets"][:4 * (self.spec.groups + 1)].view(self.torch.int32).cpu().numpy()
+        return int((np.diff(offs) > 0).sum())
+
+    def timed(self, steps, warmup, per_kernel=True):
+        torch = self.torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)] if per_kernel else None
+        # whole-step wall time without events first
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(warmup + i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        U = self.touched_groups()
+        kms = None
+        if per_kernel:
+            for i in range(steps):
+                self.step(warmup + steps + i, evs[i])
+            torch.cuda.synchronize()
+            names = ["route", "permute", "gate_up", "down", "combine"]
+            kms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
+                   for j, n in enumerate(names)}
+        return wall, U, kms
+
+
+def cpu_baseline(name, T, sample_tokens):
+    """The CPU oracle (as it stands) on a bounded sample of the workload."""
+    from gen import synth
+    from oracle import oracle
+    threads = oracle.default_threads()
+    d = synth.layer_inputs(name, sample_tokens, stream=424242)
+    t0 = time.perf_counter()
+    oracle.layer(d, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "one layer of %s on %d of its %d tokens (all routing, gate/up, down, combine steps), "
+                      "fp64 C++ oracle, %.1f s wall" % (name, sample_tokens, T, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotations", type=int, default=4, help="distinct weight sets cycled per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the int8 T=8 decode figure")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
+              "(no sharding, no collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from mixture_experts_expert_moe_amd import moe
+    moe.lib()
+
+    name, T = "bf16_e128_top8_shared", 256
+    r = Runner(name, T, args.rotations, args.steps + args.warmup)
+    wall, U, kms = r.timed(args.steps, args.warmup)
+    ms = wall / args.steps * 1e3
+    value = T / (ms / 1e3)
+    spec = r.spec
+    gu_bytes = gu_algorithmic_bytes(spec, T, U)
+    gu_ms = kms["gate_up"]
+    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+    dn_bytes = down_algorithmic_bytes(spec, T, U)
+    R = T * (spec.top_k + spec.n_shared)
+    flops = 2.0 * R * (2 * spec.inter * spec.hidden + spec.hidden * spec.inter)
+    traffic = load_traffic("gate_up", name, gu_bytes)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "grouped_gemm_kernel<bf16, gate_up>", "algorithmic_bytes_per_launch": gu_bytes,
+                "avg_launch_ms": round(gu_ms, 5)}
+    extra = {
+        "kernel_ms": {k: round(v, 5) for k, v in kms.items()},
+        "touched_groups": U,
+        "down_hbm_frac": round(dn_bytes / (kms["down"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "gemm_mfma_frac_bf16": round(flops / ((kms["gate_up"] + kms["down"]) / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                                     4),
+        "layer_hbm_frac": round((gu_bytes + dn_bytes) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        "weight_sets_rotated": args.rotations,
+    }
+    del r
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        Td = 8
+        rd = Runner("int8_e128_top8_shared", Td, max(args.rotations, 4), args.steps + args.warmup)
+        wd, Ud, kd = rd.timed(args.steps, args.warmup)
+        msd = wd / args.steps * 1e3
+        b = gu_algorithmic_bytes(rd.spec, Td, Ud) + down_algorithmic_bytes(rd.spec, Td, Ud)
+        extra["decode_int8_t8"] = {
+            "tokens_per_s": round(Td / (msd / 1e3), 1), "ms_per_step": round(msd, 5),
+            "kernel_ms": {k: round(v, 5) for k, v in kd.items()}, "touched_groups": Ud,
+            "gemm_hbm_frac": round(b / ((kd["gate_up"] + kd["down"]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemm_algorithmic_bytes": b,
+        }
+        del rd
+        torch.cuda.empty_cache()
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "tokens": T, "hidden": spec.hidden, "inter": spec.inter,
+                   "routed_experts": spec.n_routed, "top_k": spec.top_k, "shared_experts": spec.n_shared,
+                   "weights": spec.wt, "parallelism": "none (one GPU)"},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(name, T, min(args.cpu_sample, T))
+    line["extra"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

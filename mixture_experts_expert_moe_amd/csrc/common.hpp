@@ -1,0 +1,67 @@
+// Device helpers shared by the gfx950 kernels of the routed MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned u32x2;
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+
+constexpr int kWave = 64;
+
+// Layout of the tile schedule written by moe_permute (int32):
+//   [0] number of tiles, [1] groups, [2] rows,
+//   [8 + x] next work item of XCD x for the gate/up launch, [16] its exit count,
+//   [17 + x] the same for the down launch, [25] its exit count,
+//   then {group, row0, rows, 0} per tile from index kSchedHeader.
+// The GEMM launches leave their counters at zero when they finish.
+constexpr int kSchedHeader = 32;
+constexpr int kSchedGuNext = 8, kSchedGuDone = 16, kSchedDnNext = 17, kSchedDnDone = 25;
+constexpr int kTileInts = 4;
+constexpr int kTileRows = 64;     // at most 64 rows of one group per tile
+constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Plain 16-byte global loads through the vector memory path.
+template <class T>
+__device__ __forceinline__ u32x4 ld16(const T* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                  0, 0, 0);
+}
+__device__ __forceinline__ i32x4 mfma_i8_16x16x64(u32x4 a, u32x4 b, i32x4 c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0,
+                                                0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Wave-wide reductions (64 lanes) with a fixed butterfly order.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,86 @@
+// Launch interface between the C ABI (moe_api.cpp) and the kernels.  Every
+// launcher assumes its arguments were validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum WFmt { kF32 = 0, kBF16 = 1, kI8 = 2, kQ4 = 3 };
+
+struct RouteArgs {
+  const void* x;
+  const void* w_router;
+  const float* bias;
+  float* logits;
+  int32_t* topk_ids;
+  float* topk_w;
+  int T, H, E, k;
+  bool act_f32;
+};
+
+struct PermuteArgs {
+  const int32_t* topk_ids;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* token_row;
+  int32_t* sched;
+  int T, E, k, S;
+};
+
+struct QuantArgs {  // per-row symmetric int8 quantisation
+  const void* src;  // [rows][cols], bf16 bits or fp32
+  bool src_f32;
+  int8_t* q;
+  float* scale;
+  const int32_t* n_rows_dev;  // if non-null, rows = *n_rows_dev (device-resident count)
+  int rows, cols;
+};
+
+struct GemmArgs {
+  // activations: x [T][H] (gate/up) or h [R][I] (down); int8 variants in aq/as
+  const void* act;
+  const int8_t* act_q;
+  const float* act_scale;   // per token (gate/up) or per row (down)
+  const int32_t* row_token; // gate/up: row -> token; null for down (rows index act directly)
+  const int32_t* sched;
+  const void* w;
+  const void* w_scale;
+  const void* w_min;
+  void* out;                // h [R][I] (gate/up) or y [R][H] (down)
+  int K;                    // reduction length (H for gate/up, I for down)
+  int N;                    // output columns (I for gate/up, H for down)
+  int wfmt;                 // WFmt (also fixes the activation/output formats, see moe.h)
+  int T;                    // tokens (gate/up clamps row_token into [0, T))
+  int R;                    // permuted rows, T * (k + S)
+  int G;                    // groups
+};
+
+struct CombineArgs {
+  const void* y;
+  bool y_f32;
+  const int32_t* token_row;
+  const float* topk_w;
+  const float* residual;
+  void* out;
+  bool out_f32;
+  int T, H, k, S;
+};
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
+hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t stream);
+hipError_t launch_gate_up(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_down(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+hipError_t launch_rmsnorm(const float* x, uint16_t* xn, int T, int H, float eps, hipStream_t stream);
+
+// Dynamic LDS bytes the permutation kernel needs for T tokens and E experts.
+inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)((T + 63) / 64) * (size_t)E * 2; }
+constexpr size_t kPermuteMaxLds = 64 * 1024;
+
+// Capacity of the tile schedule (ints) for R_max rows over G groups.
+inline size_t sched_ints(int64_t r_max, int64_t G) { return 32 + 4 * (size_t)((r_max + 63) / 64 + G); }
+
+}  // namespace moe

@@ -1,0 +1,222 @@
+// C ABI of the routed MoE layer (include/moe.h): argument validation, buffer
+// sizing and kernel launches.  Nothing here allocates, synchronises, reads the
+// environment or keeps state; every check runs before the first launch, so an
+// error return means nothing was enqueued.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.hpp"
+
+namespace {
+
+using moe::kBF16;
+using moe::kF32;
+using moe::kI8;
+using moe::kQ4;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->hidden <= 0 || d->inter <= 0 || d->n_routed <= 0 || d->top_k <= 0 || d->max_tokens <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (d->top_k > d->n_routed || d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_INVALID_ARG;
+  if (d->hidden % 256 || d->inter % 256) return MOE_ERR_UNSUPPORTED;
+  if (d->n_routed > 256 || d->top_k > 16 || d->max_tokens > 16384) return MOE_ERR_UNSUPPORTED;
+  if (moe::permute_lds_bytes(d->max_tokens, d->n_routed) > moe::kPermuteMaxLds) return MOE_ERR_UNSUPPORTED;
+  const int a = d->act_dtype, w = d->w_dtype, o = d->out_dtype;
+  if (a < MOE_F32 || a > MOE_Q4B32 || w < MOE_F32 || w > MOE_Q4B32 || o < MOE_F32 || o > MOE_Q4B32)
+    return MOE_ERR_INVALID_ARG;
+  if (o != MOE_F32 && o != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (a == MOE_F32) {
+    if (w != MOE_F32 || o != MOE_F32) return MOE_ERR_UNSUPPORTED;
+  } else if (a == MOE_BF16) {
+    if (w == MOE_F32) return MOE_ERR_UNSUPPORTED;
+  } else {
+    return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
+// Checks shared by every per-layer call: desc, T, the buffer struct.
+moe_status check_call(const moe_desc* d, int32_t T, const moe_buffers* b) {
+  const moe_status s = check_desc(d);
+  if (s != MOE_OK) return s;
+  if (T < 0 || !b) return MOE_ERR_INVALID_ARG;
+  if (T > d->max_tokens) return MOE_ERR_BUFFER_TOO_SMALL;
+  return MOE_OK;
+}
+
+bool ptr_ok(const void* p) { return p && aligned16(p); }
+
+int groups(const moe_desc* d) { return d->n_routed + d->n_shared; }
+int64_t rows(const moe_desc* d, int64_t T) { return T * (d->top_k + d->n_shared); }
+bool f32_intermediates(const moe_desc* d) { return d->w_dtype == MOE_F32 || d->w_dtype == MOE_I8; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+moe_status check_weights(const moe_desc* d, const moe_weights* w) {
+  if (!w || !ptr_ok(w->w)) return MOE_ERR_INVALID_ARG;
+  if (d->w_dtype == MOE_I8 && !ptr_ok(w->scale)) return MOE_ERR_INVALID_ARG;
+  if (d->w_dtype == MOE_Q4B32 && (!ptr_ok(w->scale) || !ptr_ok(w->min))) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype combination";
+    case MOE_ERR_BUFFER_TOO_SMALL: return "T exceeds max_tokens";
+    case MOE_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_buffer_sizes(const moe_desc* d, size_t sizes[MOE_NUM_BUFFERS]) {
+  const moe_status s = check_desc(d);
+  if (s != MOE_OK) return s;
+  if (!sizes) return MOE_ERR_INVALID_ARG;
+  const size_t M = (size_t)d->max_tokens, E = (size_t)d->n_routed, k = (size_t)d->top_k;
+  const size_t S = (size_t)d->n_shared, H = (size_t)d->hidden, I = (size_t)d->inter;
+  const size_t G = E + S, Rmax = M * (k + S);
+  const bool i8 = d->w_dtype == MOE_I8;
+  const size_t fw = f32_intermediates(d) ? 4 : 2;
+  sizes[0] = M * E * 4;                                  // logits
+  sizes[1] = M * k * 4;                                  // topk_ids
+  sizes[2] = M * k * 4;                                  // topk_w
+  sizes[3] = (G + 1) * 4;                                // expert_offsets
+  sizes[4] = Rmax * 4;                                   // row_token
+  sizes[5] = M * (k + S) * 4;                            // token_row
+  sizes[6] = moe::sched_ints((int64_t)Rmax, (int64_t)G) * 4;  // sched
+  sizes[7] = i8 ? M * H : 0;                             // x_q
+  sizes[8] = i8 ? M * 4 : 0;                             // x_scale
+  sizes[9] = Rmax * I * fw;                              // h
+  sizes[10] = Rmax * H * fw;                             // y
+  sizes[11] = i8 ? Rmax * I : 0;                         // h_q
+  sizes[12] = i8 ? Rmax * 4 : 0;                         // h_scale
+  return MOE_OK;
+}
+
+moe_status moe_route_topk(const moe_desc* d, int32_t T, const void* x, const void* w_router, const float* bias,
+                          const moe_buffers* b, hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  if (!ptr_ok(x) || !ptr_ok(w_router) || (bias && !aligned16(bias))) return MOE_ERR_INVALID_ARG;
+  if (!ptr_ok(b->logits) || !ptr_ok(b->topk_ids) || !ptr_ok(b->topk_w)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  moe::RouteArgs a{x, w_router, bias, b->logits, b->topk_ids, b->topk_w, T, d->hidden, d->n_routed, d->top_k,
+                   d->act_dtype == MOE_F32};
+  return hip_status(moe::launch_route(a, stream));
+}
+
+moe_status moe_permute(const moe_desc* d, int32_t T, const void* x, const moe_buffers* b, hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  if (!ptr_ok(b->topk_ids) || !ptr_ok(b->expert_offsets) || !ptr_ok(b->row_token) || !ptr_ok(b->token_row) ||
+      !ptr_ok(b->sched))
+    return MOE_ERR_INVALID_ARG;
+  const bool i8 = d->w_dtype == MOE_I8;
+  if (i8 && (!ptr_ok(x) || !ptr_ok(b->x_q) || !ptr_ok(b->x_scale))) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (i8) {
+    moe::QuantArgs q{x, d->act_dtype == MOE_F32, b->x_q, b->x_scale, nullptr, T, d->hidden};
+    const hipError_t e = moe::launch_quant_rows(q, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  moe::PermuteArgs a{b->topk_ids, b->expert_offsets, b->row_token, b->token_row, b->sched, T, d->n_routed,
+                     d->top_k, d->n_shared};
+  return hip_status(moe::launch_permute(a, stream));
+}
+
+moe_status moe_grouped_gemm_gu(const moe_desc* d, int32_t T, const void* x, const moe_weights* w,
+                               const moe_buffers* b, hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(d, w)) != MOE_OK) return s;
+  const bool i8 = d->w_dtype == MOE_I8;
+  if (i8 ? (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale)) : !ptr_ok(x)) return MOE_ERR_INVALID_ARG;
+  if (!ptr_ok(b->row_token) || !ptr_ok(b->sched) || !ptr_ok(b->h)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  moe::GemmArgs a{};
+  a.act = i8 ? nullptr : x;
+  a.act_q = i8 ? b->x_q : nullptr;
+  a.act_scale = i8 ? b->x_scale : nullptr;
+  a.row_token = b->row_token;
+  a.sched = b->sched;
+  a.w = w->w;
+  a.w_scale = w->scale;
+  a.w_min = w->min;
+  a.out = b->h;
+  a.K = d->hidden;
+  a.N = d->inter;
+  a.wfmt = d->w_dtype;
+  a.T = T;
+  a.R = (int)rows(d, T);
+  a.G = groups(d);
+  return hip_status(moe::launch_gate_up(a, stream));
+}
+
+moe_status moe_grouped_gemm_down(const moe_desc* d, int32_t T, const moe_weights* w, const moe_buffers* b,
+                                 hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(d, w)) != MOE_OK) return s;
+  const bool i8 = d->w_dtype == MOE_I8;
+  if (!ptr_ok(b->h) || !ptr_ok(b->sched) || !ptr_ok(b->y)) return MOE_ERR_INVALID_ARG;
+  if (i8 && (!ptr_ok(b->h_q) || !ptr_ok(b->h_scale))) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  const int R = (int)rows(d, T);
+  if (i8) {
+    moe::QuantArgs q{b->h, true, b->h_q, b->h_scale, nullptr, R, d->inter};
+    const hipError_t e = moe::launch_quant_rows(q, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  moe::GemmArgs a{};
+  a.act = i8 ? nullptr : b->h;
+  a.act_q = i8 ? b->h_q : nullptr;
+  a.act_scale = i8 ? b->h_scale : nullptr;
+  a.row_token = nullptr;
+  a.sched = b->sched;
+  a.w = w->w;
+  a.w_scale = w->scale;
+  a.w_min = w->min;
+  a.out = b->y;
+  a.K = d->inter;
+  a.N = d->hidden;
+  a.wfmt = d->w_dtype;
+  a.T = T;
+  a.R = R;
+  a.G = groups(d);
+  return hip_status(moe::launch_down(a, stream));
+}
+
+moe_status moe_combine(const moe_desc* d, int32_t T, const float* residual, void* out, const moe_buffers* b,
+                       hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  if (!ptr_ok(out) || !ptr_ok(b->y) || !ptr_ok(b->token_row) || !ptr_ok(b->topk_w) ||
+      (residual && !aligned16(residual)))
+    return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  moe::CombineArgs a{b->y, f32_intermediates(d), b->token_row, b->topk_w, residual, out,
+                     d->out_dtype == MOE_F32, T, d->hidden, d->top_k, d->n_shared};
+  return hip_status(moe::launch_combine(a, stream));
+}
+
+moe_status moe_rmsnorm(int32_t T, int32_t H, float eps, const float* x, void* xn, hipStream_t stream) {
+  if (T < 0 || H <= 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
+  if (H % 256) return MOE_ERR_UNSUPPORTED;
+  if (!ptr_ok(x) || !ptr_ok(xn)) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  return hip_status(moe::launch_rmsnorm(x, (uint16_t*)xn, T, H, eps, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+// Router: logits, top-k selection and gates (moe_route_topk).
+//
+// The routed layer sends each token to its k highest-scoring experts and
+// weights their outputs by a softmax over those k scores ("top-8+shared" in
+// "~2.7s fixed per-request TTFT ... concatenated-expert GEMM", section "The
+// fix"; softmax placement and tie order are readings, see the header).
+//
+// Logits are accumulated in fp64 on the matrix cores (v_mfma_f64_16x16x4f64)
+// and rounded once to fp32, so the fp32 logit is the correctly rounded dot
+// product whatever the summation order.  That makes the top-k decision
+// independent of how the sum is blocked.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRouteWaves = 4;  // waves per block; each takes a quarter of H
+
+// One block computes logits for 16 tokens x 16 experts.  Lane l of a wave
+// holds token/expert (l % 16) and loads 8 consecutive h (one 16-byte load for
+// bf16, two for fp32) at h = base + 8 * (l / 16); MFMA step s of the 8 uses
+// element s, so A (x) and B (w_router) see the same permutation of K.
+template <bool kF32>
+__global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const void* __restrict__ x,
+                                                                        const void* __restrict__ wr,
+                                                                        const float* __restrict__ bias,
+                                                                        float* __restrict__ logits, int T, int H,
+                                                                        int E) {
+  __shared__ double part[kRouteWaves][16][17];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int r = lane % 16, q = lane / 16;
+  const int t = min(t0 + r, T - 1), e = min(e0 + r, E - 1);
+  const int hq = H / kRouteWaves;
+  const int hbeg = wave * hq;
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  for (int h = hbeg; h < hbeg + hq; h += 32) {
+    const int hh = h + 8 * q;
+    float xa[8], wb[8];
+    if constexpr (kF32) {
+      const float* xp = (const float*)x + (size_t)t * H + hh;
+      const float* wp = (const float*)wr + (size_t)e * H + hh;
+      const u32x4 x0 = ld16(xp), x1 = ld16(xp + 4), w0 = ld16(wp), w1 = ld16(wp + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[i] = __uint_as_float(x0[i]);
+        xa[4 + i] = __uint_as_float(x1[i]);
+        wb[i] = __uint_as_float(w0[i]);
+        wb[4 + i] = __uint_as_float(w1[i]);
+      }
+    } else {
+      const u32x4 xv = ld16((const uint16_t*)x + (size_t)t * H + hh);
+      const u32x4 wv = ld16((const uint16_t*)wr + (size_t)e * H + hh);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        xa[2 * i] = __uint_as_float(xv[i] << 16);
+        xa[2 * i + 1] = __uint_as_float(xv[i] & 0xffff0000u);
+        wb[2 * i] = __uint_as_float(wv[i] << 16);
+        wb[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[s], (double)wb[s], acc, 0, 0, 0);
+  }
+  // D layout of the f64 16x16x4 MFMA: lane l, register i holds D[4 * i + l / 16][l % 16]
+  // (row = token, column = expert) -- unlike the f32-output MFMAs, whose register i
+  // holds row 4 * (l / 16) + i.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wave][4 * i + q][r] = acc[i];
+  __syncthreads();
+  if (wave == 0) {
+    for (int idx = lane; idx < 256; idx += kWave) {
+      const int tt = idx / 16, ee = idx % 16;
+      if (t0 + tt < T && e0 + ee < E) {
+        const double s = ((part[0][tt][ee] + part[1][tt][ee]) + part[2][tt][ee]) + part[3][tt][ee];
+        float v = (float)s;
+        if (bias) v = __fadd_rn(v, bias[e0 + ee]);
+        logits[(size_t)(t0 + tt) * E + e0 + ee] = v;
+      }
+    }
+  }
+}
+
+// One wave per token: k rounds of a wave arg-max (larger logit first, equal
+// logits -> lower expert id), then the softmax of the k selected logits in fp64.
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+                                                        int32_t* __restrict__ topk_ids,
+                                                        float* __restrict__ topk_w, int T, int E, int k) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  if (t >= T) return;
+  constexpr int kPer = 4;  // E <= 256
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    v[j] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
+  }
+  unsigned taken = 0;
+  float sel_v = 0.f;
+  int sel_id = 0;
+  for (int s = 0; s < k; ++s) {
+    // best remaining in this lane (lowest id among equals: ids grow with j)
+    float bv = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + kWave * j;
+      if (e < E && !(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bid))) {
+        bv = v[j];
+        bid = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oid = __shfl_xor(bid, o, kWave);
+      if (ov > bv || (ov == bv && oid < bid)) {
+        bv = ov;
+        bid = oid;
+      }
+    }
+    if ((bid % kWave) == lane) taken |= 1u << (bid / kWave);
+    if (lane == s) {
+      sel_v = bv;
+      sel_id = bid;
+    }
+  }
+  // Gates: softmax over the selected logits, fp64, slot order, rounded once.
+  const double top = (double)__shfl(sel_v, 0, kWave);
+  const double ex = lane < k ? exp((double)sel_v - top) : 0.0;
+  double den = 0.0;
+  for (int s = 0; s < k; ++s) den += __shfl(ex, s, kWave);
+  if (lane < k) {
+    topk_ids[(size_t)t * k + lane] = sel_id;
+    topk_w[(size_t)t * k + lane] = (float)(ex / den);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  dim3 grid((a.T + 15) / 16, (a.E + 15) / 16);
+  if (a.act_f32)
+    hipLaunchKernelGGL(route_logits_kernel<true>, grid, dim3(kWave * kRouteWaves), 0, stream, a.x, a.w_router,
+                       a.bias, a.logits, a.T, a.H, a.E);
+  else
+    hipLaunchKernelGGL(route_logits_kernel<false>, grid, dim3(kWave * kRouteWaves), 0, stream, a.x, a.w_router,
+                       a.bias, a.logits, a.T, a.H, a.E);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, a.topk_ids, a.topk_w,
+                     a.T, a.E, a.k);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,118 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/moe.h declares, sizes buffers, and rejects bad arguments before any
+launch (only rejected calls are made here; nothing reaches a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_expert_moe_amd import moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS), names
+    L = moe.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moe_abi_version() == 1
+
+
+def test_status_strings():
+    L = moe.lib()
+    for code in (0, -1, -2, -3, -4):
+        assert L.moe_status_string(code)
+
+
+def bufs_all(p=FAKE):
+    return moe.MoeBuffers(*([p] * len(moe.BUFFER_NAMES)))
+
+
+def desc(**kw):
+    base = dict(hidden=2048, inter=512, n_routed=128, top_k=8, n_shared=1, max_tokens=256, act="bf16", wt="bf16",
+                out="bf16")
+    base.update(kw)
+    return moe.make_desc(**base)
+
+
+def status(fn, *args):
+    return getattr(moe.lib(), fn)(*args)
+
+
+def test_buffer_sizes_match_shapes():
+    s = moe.moe_buffer_sizes(desc())
+    R = 256 * 9
+    assert s["logits"] == 256 * 128 * 4
+    assert s["topk_ids"] == s["topk_w"] == 256 * 8 * 4
+    assert s["expert_offsets"] == 130 * 4
+    assert s["row_token"] == R * 4 and s["token_row"] == 256 * 9 * 4
+    assert s["h"] == R * 512 * 2 and s["y"] == R * 2048 * 2
+    assert s["x_q"] == s["h_q"] == 0
+    s8 = moe.moe_buffer_sizes(desc(wt="i8"))
+    assert s8["x_q"] == 256 * 2048 and s8["h_q"] == R * 512 and s8["h"] == R * 512 * 4
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hidden=2000), -2), (dict(inter=300), -2), (dict(top_k=0), -1), (dict(top_k=129), -1),
+    (dict(top_k=17, n_routed=32), -2), (dict(n_shared=2), -1), (dict(max_tokens=0), -1),
+    (dict(max_tokens=20000), -2), (dict(n_routed=257, top_k=8), -2), (dict(act="f32", wt="bf16"), -2),
+    (dict(act="bf16", wt="f32"), -2), (dict(out="i8"), -2), (dict(act="i8"), -2),
+    (dict(n_routed=256, max_tokens=16384), -2),
+])
+def test_bad_desc_rejected(kw, code):
+    sizes = (ctypes.c_size_t * 13)()
+    assert status("moe_buffer_sizes", ctypes.byref(desc(**kw)), sizes) == code
+
+
+def test_calls_reject_before_launch():
+    d = desc()
+    b = bufs_all()
+    w = moe.MoeWeights(FAKE, None, None)
+    by = ctypes.byref
+    # T > max_tokens
+    assert status("moe_route_topk", by(d), 257, FAKE, FAKE, None, by(b), None) == -3
+    assert status("moe_permute", by(d), 300, FAKE, by(b), None) == -3
+    assert status("moe_grouped_gemm_gu", by(d), 257, FAKE, by(w), by(b), None) == -3
+    assert status("moe_grouped_gemm_down", by(d), 257, by(w), by(b), None) == -3
+    assert status("moe_combine", by(d), 257, None, FAKE, by(b), None) == -3
+    # negative T, null pointers, misaligned pointers, missing quantisation parameters
+    assert status("moe_route_topk", by(d), -1, FAKE, FAKE, None, by(b), None) == -1
+    assert status("moe_route_topk", by(d), 4, None, FAKE, None, by(b), None) == -1
+    assert status("moe_route_topk", by(d), 4, FAKE + 2, FAKE, None, by(b), None) == -1
+    assert status("moe_grouped_gemm_gu", by(d), 4, FAKE, by(moe.MoeWeights(None, None, None)), by(b), None) == -1
+    d8 = desc(wt="i8")
+    assert status("moe_grouped_gemm_gu", by(d8), 4, FAKE, by(w), by(b), None) == -1       # no scales
+    d4 = desc(wt="q4")
+    assert status("moe_grouped_gemm_down", by(d4), 4, by(moe.MoeWeights(FAKE, FAKE, None)), by(b), None) == -1
+    nob = bufs_all(None)
+    assert status("moe_permute", by(d), 4, FAKE, by(nob), None) == -1
+    assert status("moe_combine", by(d), 4, None, FAKE, by(nob), None) == -1
+    assert status("moe_rmsnorm", 4, 2000, ctypes.c_float(1e-6), FAKE, FAKE, None) == -2
+    assert status("moe_rmsnorm", -1, 2048, ctypes.c_float(1e-6), FAKE, FAKE, None) == -1
+    # bad desc through a compute call
+    assert status("moe_combine", by(desc(hidden=100)), 4, None, FAKE, by(b), None) == -2
+
+
+def test_zero_tokens_returns_ok_without_launch():
+    d = desc()
+    b = bufs_all()
+    w = moe.MoeWeights(FAKE, None, None)
+    by = ctypes.byref
+    assert status("moe_route_topk", by(d), 0, FAKE, FAKE, None, by(b), None) == 0
+    assert status("moe_permute", by(d), 0, FAKE, by(b), None) == 0
+    assert status("moe_grouped_gemm_gu", by(d), 0, FAKE, by(w), by(b), None) == 0
+    assert status("moe_grouped_gemm_down", by(d), 0, by(w), by(b), None) == 0
+    assert status("moe_combine", by(d), 0, None, FAKE, by(b), None) == 0
+    assert status("moe_rmsnorm", 0, 2048, ctypes.c_float(1e-6), FAKE, FAKE, None) == 0
