@@ -169,18 +169,21 @@ class Runner:
         return wall, U, kms
 
 
-def cpu_baseline(name, T, sample_tokens):
-    """The CPU oracle (as it stands) on a bounded sample of the workload."""
+def cpu_baseline(name, T, sample_tokens, batches=3):
+    """The CPU oracle (as it stands) on a bounded sample of the workload: `batches`
+    distinct token batches of `sample_tokens` tokens through one layer."""
     from gen import synth
     from oracle import oracle
     threads = oracle.default_threads()
-    d = synth.layer_inputs(name, sample_tokens, stream=424242)
+    inputs = [synth.layer_inputs(name, sample_tokens, stream=424242 + b) for b in range(batches)]
     t0 = time.perf_counter()
-    oracle.layer(d, threads=threads)
+    for d in inputs:
+        oracle.layer(d, threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": "one layer of %s on %d of its %d tokens (all routing, gate/up, down, combine steps), "
-                      "fp64 C++ oracle, %.1f s wall" % (name, sample_tokens, T, dt)}
+    return {"value": batches * sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d batches of %d tokens (of the %d-token workload %s), each through one whole layer "
+                      "(routing, permutation, gate/up, down, combine), fp64 C++ oracle, %.1f s wall on %d threads"
+                      % (batches, sample_tokens, T, name, dt, threads)}
 
 
 def main():
@@ -192,6 +195,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the int8 T=8 decode figure")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a reference kernel of known "
+                         "size for hardware-counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -203,6 +209,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     from mixture_experts_expert_moe_amd import moe
     moe.lib()
+    if args.copy_calib_mb:
+        n = args.copy_calib_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copy of %d MiB done" % args.copy_calib_mb)
+        del src, dst
 
     name, T = "bf16_e128_top8_shared", 256
     r = Runner(name, T, args.rotations, args.steps + args.warmup)

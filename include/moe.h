@@ -81,9 +81,10 @@ typedef enum moe_dtype {
  *   (BF16, I8, BF16 or F32)    x quantised per token to int8 inside moe_permute
  *   (BF16, Q4B32, BF16 or F32) 4-bit weights dequantised to bf16 in registers
  * Limits: hidden % 256 == 0, inter % 256 == 0, 1 <= n_routed <= 256,
- * 1 <= top_k <= min(16, n_routed), n_shared in {0, 1}, 1 <= max_tokens <= 16384
- * and ceil(max_tokens / 64) * n_routed <= 32768 (the permutation keeps one
- * 16-bit count per 64-token chunk and expert in LDS). */
+ * 1 <= top_k <= min(16, n_routed), n_shared in {0, 1}, max_tokens >= 1 and
+ * 6 * n_routed * ceil(max_tokens / 32) <= 61440 (the permutation keeps a token
+ * bitmap and a 16-bit prefix per expert in LDS: max_tokens <= 2560 for 128
+ * experts). */
 typedef struct moe_desc {
   int32_t hidden;      /* H: model width (2048 in the pages' model) */
   int32_t inter;       /* I: expert intermediate width (512) */

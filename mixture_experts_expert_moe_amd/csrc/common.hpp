@@ -17,13 +17,9 @@ typedef __attribute__((ext_vector_type(4))) double f64x4;
 constexpr int kWave = 64;
 
 // Layout of the tile schedule written by moe_permute (int32):
-//   [0] number of tiles, [1] groups, [2] rows,
-//   [8 + x] next work item of XCD x for the gate/up launch, [16] its exit count,
-//   [17 + x] the same for the down launch, [25] its exit count,
+//   [0] number of tiles, [1] groups, [2] rows, [3..31] zero (reserved),
 //   then {group, row0, rows, 0} per tile from index kSchedHeader.
-// The GEMM launches leave their counters at zero when they finish.
 constexpr int kSchedHeader = 32;
-constexpr int kSchedGuNext = 8, kSchedGuDone = 16, kSchedDnNext = 17, kSchedDnDone = 25;
 constexpr int kTileInts = 4;
 constexpr int kTileRows = 64;     // at most 64 rows of one group per tile
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, workgroups dealt round-robin

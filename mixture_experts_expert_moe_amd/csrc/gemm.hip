@@ -10,10 +10,9 @@
 // 2026-10-27 trace comment).  The shared expert is one more group of the same
 // launch, as the fused "gate_up_shared" / "silu_down_shared" kernels there do.
 //
-// Work item = (tile of <= 64 rows of one group) x (16 output columns).  A
-// workgroup is one wave; it takes items from a per-XCD counter (items of one
-// XCD are a contiguous range, so the rows of a tile stay in that XCD's L2),
-// then steals from the other XCDs.  Within an item:
+// Work item = (tile of <= 64 rows of one group) x (32 gate/up pairs, or 64
+// down columns); one workgroup per item, its waves splitting K.
+// Within an item:
 //   MFMA A operand = 16 weight rows (lane l: row l % 16, K-group l / 16),
 //   MFMA B operand = 16 token rows  (lane l: row l % 16, same K-group),
 //   D[i][j] lands in lane j + 16 * (i / 4), register i % 4, so a lane owns four
@@ -29,22 +28,35 @@ namespace {
 
 template <int WF>
 struct FmtTraits;
-// KS: K elements one stage covers; U: stages per batch of loads.
+// KS: K elements one stage covers (4 lane groups x one 16-byte load per lane).
 template <>
-struct FmtTraits<kBF16> { static constexpr int KS = 32, U = 8; };
+struct FmtTraits<kBF16> { static constexpr int KS = 32; };
 template <>
-struct FmtTraits<kF32> { static constexpr int KS = 16, U = 8; };
+struct FmtTraits<kF32> { static constexpr int KS = 16; };
 template <>
-struct FmtTraits<kI8> { static constexpr int KS = 64, U = 4; };
+struct FmtTraits<kI8> { static constexpr int KS = 64; };
 template <>
-struct FmtTraits<kQ4> { static constexpr int KS = 128, U = 2; };
+struct FmtTraits<kQ4> { static constexpr int KS = 128; };
+
+// Stages per batch: a batch is what one wave keeps in flight while it computes
+// the previous one.  Fewer stages for tall tiles keeps the B registers bounded.
+#ifndef MOE_STAGES_SMALL
+#define MOE_STAGES_SMALL 4
+#endif
+#ifndef MOE_STAGES_LARGE
+#define MOE_STAGES_LARGE 2
+#endif
+template <int WF, int NSUB>
+constexpr int stages() {
+  return WF == kQ4 ? 1 : (NSUB <= 2 ? MOE_STAGES_SMALL : MOE_STAGES_LARGE);
+}
 
 struct Kp {  // kernel parameters
   const void* act;
   const int8_t* act_q;
   const float* act_scale;
   const int32_t* row_token;
-  int32_t* sched;
+  const int32_t* sched;
   const void* w;
   const void* w_scale;
   const void* w_min;
@@ -56,7 +68,8 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }
 
-// Eight 4-bit codes (one 32-bit word, code n at bits 4n) -> 8 bf16 of scale * q + min.
+// Eight 4-bit codes (one 32-bit word, code n at bits 4n) -> 8 bf16 of scale * q + min
+// (q * scale is exact in fp32, so the fma rounds once, like scale * q + min).
 __device__ __forceinline__ u32x4 dequant8(uint32_t w, float sc, float mn) {
   const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
   u32x4 r;
@@ -69,15 +82,14 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float sc, float mn) {
   return r;
 }
 
-// Weight operand of one stage for one weight row (A operand).
-template <int WF>
+// Weight operand of one stage for one 16-row block (A operand).
 struct AStage {
-  u32x4 v;            // raw 16 bytes
-  float sc = 0, mn = 0;  // 4-bit block parameters
+  u32x4 v;               // raw 16 bytes
+  float sc, mn;          // 4-bit block parameters
 };
 
 template <int WF>
-__device__ __forceinline__ void load_a(AStage<WF>& s, const Kp& p, size_t wrow, int k0, int q) {
+__device__ __forceinline__ void load_a(AStage& s, const Kp& p, size_t wrow, int k0, int q) {
   if constexpr (WF == kBF16) {
     s.v = ld16((const uint16_t*)p.w + wrow * p.K + k0 + 8 * q);
   } else if constexpr (WF == kF32) {
@@ -85,6 +97,7 @@ __device__ __forceinline__ void load_a(AStage<WF>& s, const Kp& p, size_t wrow, 
   } else if constexpr (WF == kI8) {
     s.v = ld16((const int8_t*)p.w + wrow * p.K + k0 + 16 * q);
   } else {
+    // lane group q holds the whole 32-code block k0/32 + q
     s.v = ld16((const uint8_t*)p.w + wrow * (size_t)(p.K / 2) + k0 / 2 + 16 * q);
     const size_t b = wrow * (size_t)(p.K / 32) + k0 / 32 + q;
     s.sc = half_bits_to_f32(((const uint16_t*)p.w_scale)[b]);
@@ -92,7 +105,7 @@ __device__ __forceinline__ void load_a(AStage<WF>& s, const Kp& p, size_t wrow, 
   }
 }
 
-// Activation operand of one stage for one token row (B operand).
+// Activation operand of one stage for one 16-row block (B operand).
 template <int WF>
 struct BStage {
   u32x4 v[WF == kQ4 ? 4 : 1];
@@ -115,18 +128,34 @@ __device__ __forceinline__ void load_b(BStage<WF>& s, const Kp& p, size_t arow, 
 template <int WF>
 using Acc = typename std::conditional<WF == kI8, i32x4, f32x4>::type;
 
-template <int WF>
-__device__ __forceinline__ void mma(Acc<WF>& c, const AStage<WF>& a, const BStage<WF>& b) {
-  if constexpr (WF == kBF16) {
-    c = mfma_bf16_16x16x32(a.v, b.v[0], c);
-  } else if constexpr (WF == kF32) {
+// One stage: NA weight blocks x NSUB token blocks.
+template <int WF, int NA, int NSUB>
+__device__ __forceinline__ void mma_stage(Acc<WF> (&acc)[NA][NSUB], const AStage (&a)[NA],
+                                          const BStage<WF> (&b)[NSUB]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) c = mfma_f32_16x16x4(__uint_as_float(a.v[j]), __uint_as_float(b.v[0][j]), c);
-  } else if constexpr (WF == kI8) {
-    c = mfma_i8_16x16x64(a.v, b.v[0], c);
-  } else {
+  for (int n = 0; n < NA; ++n) {
+    if constexpr (WF == kQ4) {
+      u32x4 w[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) c = mfma_bf16_16x16x32(dequant8(a.v[m], a.sc, a.mn), b.v[m], c);
+      for (int m = 0; m < 4; ++m) w[m] = dequant8(a[n].v[m], a[n].sc, a[n].mn);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) acc[n][s] = mfma_bf16_16x16x32(w[m], b[s].v[m], acc[n][s]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) {
+        if constexpr (WF == kBF16) {
+          acc[n][s] = mfma_bf16_16x16x32(a[n].v, b[s].v[0], acc[n][s]);
+        } else if constexpr (WF == kF32) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[n][s] = mfma_f32_16x16x4(__uint_as_float(a[n].v[j]), __uint_as_float(b[s].v[0][j]), acc[n][s]);
+        } else {
+          acc[n][s] = mfma_i8_16x16x64(a[n].v, b[s].v[0], acc[n][s]);
+        }
+      }
+    }
   }
 }
 
@@ -139,31 +168,8 @@ __device__ __forceinline__ float silu_exact(float g) {
   return __fdiv_rn(g, __fadd_rn(1.0f, e));
 }
 
-template <int WF, bool kGU>
-__device__ __forceinline__ void store_out(const Kp& p, int r, int col, const Acc<WF>& g_acc, const Acc<WF>& u_acc,
-                                          int group, int tok) {
-  float v[4];
-  if constexpr (WF == kI8) {
-    if constexpr (kGU) {
-      const float xs = p.act_scale[tok];
-      const float* ws = (const float*)p.w_scale + (size_t)group * 2 * p.N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float ag = __fmul_rn(__fmul_rn((float)g_acc[i], xs), ws[col + i]);
-        const float au = __fmul_rn(__fmul_rn((float)u_acc[i], xs), ws[p.N + col + i]);
-        v[i] = __fmul_rn(silu_exact(ag), au);
-      }
-    } else {
-      const float hs = p.act_scale[r];
-      const float* ws = (const float*)p.w_scale + (size_t)group * p.N;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = __fmul_rn(__fmul_rn((float)g_acc[i], hs), ws[col + i]);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = kGU ? silu_fast(g_acc[i]) * u_acc[i] : g_acc[i];
-  }
-  if constexpr (WF == kF32 || WF == kI8) {
+__device__ __forceinline__ void store4(const Kp& p, bool f32, int r, int col, const float v[4]) {
+  if (f32) {
     f32x4 o = {v[0], v[1], v[2], v[3]};
     *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = o;
   } else {
@@ -172,14 +178,81 @@ __device__ __forceinline__ void store_out(const Kp& p, int r, int col, const Acc
   }
 }
 
+// Gate/up epilogue: SwiGLU of the pair (gate block, up block); lane owns
+// output columns col .. col+3 of row r.
+template <int WF>
+__device__ __forceinline__ void store_gu(const Kp& p, int r, int col, const Acc<WF>& g, const Acc<WF>& u, int group,
+                                         int tok) {
+  float v[4];
+  if constexpr (WF == kI8) {
+    const float xs = p.act_scale[tok];
+    const float* ws = (const float*)p.w_scale + (size_t)group * 2 * p.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float ag = __fmul_rn(__fmul_rn((float)g[i], xs), ws[col + i]);
+      const float au = __fmul_rn(__fmul_rn((float)u[i], xs), ws[p.N + col + i]);
+      v[i] = __fmul_rn(silu_exact(ag), au);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = silu_fast(g[i]) * u[i];
+  }
+  store4(p, WF == kF32 || WF == kI8, r, col, v);
+}
+
+template <int WF>
+__device__ __forceinline__ void store_down(const Kp& p, int r, int col, const Acc<WF>& y, int group) {
+  float v[4];
+  if constexpr (WF == kI8) {
+    const float hs = p.act_scale[r];
+    const float* ws = (const float*)p.w_scale + (size_t)group * p.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __fmul_rn(__fmul_rn((float)y[i], hs), ws[col + i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = y[i];
+  }
+  store4(p, WF == kF32 || WF == kI8, r, col, v);
+}
+
+constexpr int kItemBlocks = 4;  // 16-row weight blocks per work item
+
+#ifndef MOE_SPLIT_GU
+#define MOE_SPLIT_GU 4
+#endif
+#ifndef MOE_SPLIT_DN
+#define MOE_SPLIT_DN 2
+#endif
+// Waves per workgroup; they split an item's K range.
+template <bool kGU>
+constexpr int split() { return kGU ? MOE_SPLIT_GU : MOE_SPLIT_DN; }
+
+// One work item: rows [row0, row0 + rows) of one group against four 16-row
+// weight blocks: gate rows n0.., n0+16.. and up rows n0.., n0+16.. of the
+// group for gate/up (32 output columns), or output columns n0 .. n0+63 for
+// down.  Each activation fragment feeds all four blocks.  The four waves of the workgroup take
+// consecutive quarters of the K batches; each walks its quarter in batches of
+// U stages with the next batch's loads in flight while the current one
+// computes.  Partial sums meet in LDS and are added in wave order
+// ((w0 + w1) + w2) + w3, so the result does not depend on scheduling.
 template <int WF, bool kGU, int NSUB>
-__device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int rows, int n0) {
-  using Tr = FmtTraits<WF>;
-  const int lane = threadIdx.x;
+__device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int rows, int n0, Acc<WF>* red) {
+  constexpr int KS = FmtTraits<WF>::KS;
+  constexpr int U = stages<WF, NSUB>();
+  constexpr int KB = KS * U;
+  constexpr int NA = kItemBlocks;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int lr = lane % 16, q = lane / 16;
-  // Weight rows: gate/up -> W[g][n0 + lr] and W[g][N + n0 + lr] of [G][2N][K]; down -> W[g][n0 + lr] of [G][N][K].
-  const size_t wrow_g = kGU ? (size_t)group * 2 * p.N + n0 + lr : (size_t)group * p.N + n0 + lr;
-  const size_t wrow_u = wrow_g + p.N;
+  size_t wrow[NA];
+  if constexpr (kGU) {
+    wrow[0] = (size_t)group * 2 * p.N + n0 + lr;  // gate rows
+    wrow[1] = wrow[0] + 16;
+    wrow[2] = wrow[0] + p.N;                      // up rows
+    wrow[3] = wrow[1] + p.N;
+  } else {
+#pragma unroll
+    for (int n = 0; n < NA; ++n) wrow[n] = (size_t)group * p.N + n0 + 16 * n + lr;
+  }
   size_t arow[NSUB];
   int tok[NSUB];
 #pragma unroll
@@ -193,102 +266,126 @@ __device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int 
       arow[s] = (size_t)rr;
     }
   }
-  Acc<WF> acc_g[NSUB], acc_u[NSUB];
+  Acc<WF> acc[NA][NSUB];
+#pragma unroll
+  for (int n = 0; n < NA; ++n)
+#pragma unroll
+    for (int s = 0; s < NSUB; ++s) acc[n][s] = Acc<WF>{0, 0, 0, 0};
+
+  AStage a0[U][NA], a1[U][NA];
+  BStage<WF> b0[U][NSUB], b1[U][NSUB];
+  auto load = [&](AStage (&a)[U][NA], BStage<WF> (&b)[U][NSUB], int kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int n = 0; n < NA; ++n) load_a<WF>(a[u][n], p, wrow[n], kb + u * KS, q);
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) load_b<WF>(b[u][s], p, arow[s], kb + u * KS, q);
+    }
+  };
+  auto compute = [&](const AStage (&a)[U][NA], const BStage<WF> (&b)[U][NSUB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) mma_stage<WF, NA, NSUB>(acc, a[u], b[u]);
+  };
+  // The waves' K ranges are cut in units of the largest batch (a one-block
+  // tile's), the same for every tile height, so a row's partial sums never
+  // depend on the tile it falls in; a wave walks its range in batches of KB.
+  constexpr int KP = KS * stages<WF, 1>();
+  static_assert(KP % KB == 0, "batch must divide the partition unit");
+  constexpr int kSplit = split<kGU>();
+  const int units = p.K / KP;
+  const int ubeg = wave * units / kSplit, uend = (wave + 1) * units / kSplit;
+  const int nb = (uend - ubeg) * (KP / KB);
+  const int kbase = ubeg * KP;
+  if (nb > 0) load(a0, b0, kbase);
+  for (int i = 0; i < nb; i += 2) {
+    if (i + 1 < nb) load(a1, b1, kbase + (i + 1) * KB);
+    compute(a0, b0);
+    if (i + 2 < nb) load(a0, b0, kbase + (i + 2) * KB);
+    if (i + 1 < nb) compute(a1, b1);
+  }
+  // Cross-wave reduction: waves 1..3 park their partials, wave 0 adds them in order.
+  if (wave > 0) {
+#pragma unroll
+    for (int n = 0; n < NA; ++n)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) red[(((wave - 1) * NA + n) * NSUB + s) * kWave + lane] = acc[n][s];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < kSplit; ++w)
+#pragma unroll
+    for (int n = 0; n < NA; ++n)
+#pragma unroll
+      for (int s = 0; s < NSUB; ++s) acc[n][s] += red[(((w - 1) * NA + n) * NSUB + s) * kWave + lane];
+  // D[i][j] of block (n, s) is in lane j + 16 * (i / 4), register i % 4:
+  // this lane holds columns 4q .. 4q+3 of the block for row 16 s + lr.
 #pragma unroll
   for (int s = 0; s < NSUB; ++s) {
-    acc_g[s] = Acc<WF>{0, 0, 0, 0};
-    acc_u[s] = Acc<WF>{0, 0, 0, 0};
-  }
-  for (int kb = 0; kb < p.K; kb += Tr::KS * Tr::U) {
-    AStage<WF> ag[Tr::U], au[Tr::U];
-    BStage<WF> b[Tr::U][NSUB];
+    if (16 * s + lr < rows) {
+      const int r = row0 + 16 * s + lr;
+      if constexpr (kGU) {
+        store_gu<WF>(p, r, n0 + 4 * q, acc[0][s], acc[2][s], group, tok[s]);
+        store_gu<WF>(p, r, n0 + 16 + 4 * q, acc[1][s], acc[3][s], group, tok[s]);
+      } else {
 #pragma unroll
-    for (int u = 0; u < Tr::U; ++u) {
-      const int k0 = kb + u * Tr::KS;
-      load_a<WF>(ag[u], p, wrow_g, k0, q);
-      if constexpr (kGU) load_a<WF>(au[u], p, wrow_u, k0, q);
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) load_b<WF>(b[u][s], p, arow[s], k0, q);
-    }
-#pragma unroll
-    for (int u = 0; u < Tr::U; ++u) {
-#pragma unroll
-      for (int s = 0; s < NSUB; ++s) {
-        mma<WF>(acc_g[s], ag[u], b[u][s]);
-        if constexpr (kGU) mma<WF>(acc_u[s], au[u], b[u][s]);
+        for (int n = 0; n < NA; ++n) store_down<WF>(p, r, n0 + 16 * n + 4 * q, acc[n][s], group);
       }
     }
   }
-  // Lane owns output columns n0 + 4q .. n0 + 4q + 3 of row row0 + 16 s + lr.
-#pragma unroll
-  for (int s = 0; s < NSUB; ++s) {
-    if (16 * s + lr < rows) store_out<WF, kGU>(p, row0 + 16 * s + lr, n0 + 4 * q, acc_g[s], acc_u[s], group, tok[s]);
-  }
 }
+
+// Output columns one work item covers: 32 gate/up pairs, or 64 down columns.
+template <bool kGU>
+constexpr int item_cols() { return kGU ? 32 : 64; }
+
+// One launch over (tile x column block) items; the grid is sized on the host
+// from an upper bound and each workgroup takes one item, in schedule order
+// (heaviest tiles first).  Workgroup b runs on XCD b % 8, so the column blocks
+// of every tile are spread evenly over the eight XCDs.
+#ifndef MOE_GEMM_WAVES_PER_SIMD
+#define MOE_GEMM_WAVES_PER_SIMD 2
+#endif
+// Occupancy target: two waves per SIMD keeps enough loads in flight; the
+// 4-bit path needs more registers for its dequantised operands.
+template <int WF>
+constexpr int waves_per_simd() { return WF == kQ4 ? 1 : MOE_GEMM_WAVES_PER_SIMD; }
 
 template <int WF, bool kGU>
-__global__ __launch_bounds__(kWave) void grouped_gemm_kernel(Kp p) {
+__global__ __launch_bounds__(kWave* split<kGU>()) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WF>())))
+void grouped_gemm_kernel(Kp p) {
+  __shared__ Acc<WF> red[(split<kGU>() > 1 ? split<kGU>() - 1 : 1) * kItemBlocks * 4 * kWave];
   const int n_tiles = p.sched[0];
-  const int nt_per_tile = p.N / 16;
-  const int total = n_tiles * nt_per_tile;
-  int* next = p.sched + (kGU ? kSchedGuNext : kSchedDnNext);
-  int* done = p.sched + (kGU ? kSchedGuDone : kSchedDnDone);
-  const int per = (total + kXcds - 1) / kXcds;
-  const int home = blockIdx.x % kXcds;
-  const int lane = threadIdx.x;
-  for (int xi = 0; xi < kXcds; ++xi) {
-    const int x = (home + xi) % kXcds;
-    const int beg = x * per, end = min(total, beg + per);
-    while (true) {
-      int w = 0;
-      if (lane == 0) w = atomicAdd(next + x, 1);
-      w = __shfl(w, 0, kWave) + beg;
-      if (w >= end) break;
-      const int mt = w / nt_per_tile, nt = w % nt_per_tile;
-      const int32_t* tile = p.sched + kSchedHeader + (size_t)mt * kTileInts;
-      const int group = tile[0], row0 = tile[1], rows = tile[2];
-      const int n0 = nt * 16;
-      switch ((rows + 15) / 16) {
-        case 1: gemm_item<WF, kGU, 1>(p, group, row0, rows, n0); break;
-        case 2: gemm_item<WF, kGU, 2>(p, group, row0, rows, n0); break;
-        case 3: gemm_item<WF, kGU, 3>(p, group, row0, rows, n0); break;
-        default: gemm_item<WF, kGU, 4>(p, group, row0, rows, n0); break;
-      }
-    }
+  const int per_tile = p.N / item_cols<kGU>();
+  const int total = n_tiles * per_tile;
+  const int w = blockIdx.x;
+  if (w >= total) return;
+  const int mt = w / per_tile, nt = w % per_tile;
+  const int32_t* tile = p.sched + kSchedHeader + (size_t)mt * kTileInts;
+  const int group = tile[0], row0 = tile[1], rows = tile[2];
+  const int n0 = nt * item_cols<kGU>();
+  switch ((rows + 15) / 16) {
+    case 1: gemm_item<WF, kGU, 1>(p, group, row0, rows, n0, red); break;
+    case 2: gemm_item<WF, kGU, 2>(p, group, row0, rows, n0, red); break;
+    case 3: gemm_item<WF, kGU, 3>(p, group, row0, rows, n0, red); break;
+    default: gemm_item<WF, kGU, 4>(p, group, row0, rows, n0, red); break;
   }
-  // The last workgroup out resets the counters for the next launch.
-  __threadfence();
-  if (lane == 0) {
-    const int d = atomicAdd(done, 1);
-    if (d == (int)gridDim.x - 1) {
-      for (int x = 0; x < kXcds; ++x) atomicExch(next + x, 0);
-      atomicExch(done, 0);
-    }
-  }
-}
-
-int grid_for(const GemmArgs& a, int items_bound) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
-  int grid = std::min(items_bound, cus * 8);
-  grid = std::max(kXcds, (grid + kXcds - 1) / kXcds * kXcds);
-  return grid;
 }
 
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
-  Kp p{a.act, a.act_q, a.act_scale, a.row_token, const_cast<int32_t*>(a.sched), a.w, a.w_scale, a.w_min,
-       a.out, a.K, a.N, a.T, a.R};
+  Kp p{a.act, a.act_q, a.act_scale, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
   // Upper bound on tiles: every non-empty group adds at most one partial tile.
-  const int64_t tiles = (a.R + 63) / 64 + std::min<int64_t>(a.G, a.R);
-  const int grid = grid_for(a, (int)std::min<int64_t>(tiles * (a.N / 16), 1 << 30));
+  const int64_t tiles = (a.R + kTileRows - 1) / kTileRows + std::min<int64_t>(a.G, a.R);
+  const int64_t items = tiles * (a.N / item_cols<kGU>());
+  const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
+  if (grid <= 0 || grid > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   switch (a.wfmt) {
-    case kF32: hipLaunchKernelGGL((grouped_gemm_kernel<kF32, kGU>), dim3(grid), dim3(kWave), 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((grouped_gemm_kernel<kBF16, kGU>), dim3(grid), dim3(kWave), 0, stream, p); break;
-    case kI8: hipLaunchKernelGGL((grouped_gemm_kernel<kI8, kGU>), dim3(grid), dim3(kWave), 0, stream, p); break;
-    case kQ4: hipLaunchKernelGGL((grouped_gemm_kernel<kQ4, kGU>), dim3(grid), dim3(kWave), 0, stream, p); break;
+    case kF32: hipLaunchKernelGGL((grouped_gemm_kernel<kF32, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
+    case kBF16: hipLaunchKernelGGL((grouped_gemm_kernel<kBF16, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
+    case kI8: hipLaunchKernelGGL((grouped_gemm_kernel<kI8, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
+    case kQ4: hipLaunchKernelGGL((grouped_gemm_kernel<kQ4, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -76,9 +76,10 @@ hipError_t launch_down(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, uint16_t* xn, int T, int H, float eps, hipStream_t stream);
 
-// Dynamic LDS bytes the permutation kernel needs for T tokens and E experts.
-inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)((T + 63) / 64) * (size_t)E * 2; }
-constexpr size_t kPermuteMaxLds = 64 * 1024;
+// Dynamic LDS bytes the permutation kernel needs for T tokens and E experts:
+// a 32-bit word of token bits plus a 16-bit prefix per (expert, 32 tokens).
+inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)((T + 31) / 32) * (size_t)E * 6; }
+constexpr size_t kPermuteMaxLds = 60 * 1024;
 
 // Capacity of the tile schedule (ints) for R_max rows over G groups.
 inline size_t sched_ints(int64_t r_max, int64_t G) { return 32 + 4 * (size_t)((r_max + 63) / 64 + G); }

@@ -23,7 +23,7 @@ moe_status check_desc(const moe_desc* d) {
     return MOE_ERR_INVALID_ARG;
   if (d->top_k > d->n_routed || d->n_shared < 0 || d->n_shared > 1) return MOE_ERR_INVALID_ARG;
   if (d->hidden % 256 || d->inter % 256) return MOE_ERR_UNSUPPORTED;
-  if (d->n_routed > 256 || d->top_k > 16 || d->max_tokens > 16384) return MOE_ERR_UNSUPPORTED;
+  if (d->n_routed > 256 || d->top_k > 16) return MOE_ERR_UNSUPPORTED;
   if (moe::permute_lds_bytes(d->max_tokens, d->n_routed) > moe::kPermuteMaxLds) return MOE_ERR_UNSUPPORTED;
   const int a = d->act_dtype, w = d->w_dtype, o = d->out_dtype;
   if (a < MOE_F32 || a > MOE_Q4B32 || w < MOE_F32 || w > MOE_Q4B32 || o < MOE_F32 || o > MOE_Q4B32)

@@ -6,13 +6,17 @@
 // sections "Evidence" and "The fix"; "eight tokens through each expert in one
 // go", OpenFlowLM-Next issue #74).
 //
-// One workgroup of 16 waves.  Tokens are taken in chunks of 64 (lane = token).
-// Pass 1: each wave finds, for every expert present in its chunk, the ballot
-// of lanes that chose it; a lane's rank inside the chunk is the popcount of
-// that ballot below its lane, the chunk's count its full popcount.  Pass 2:
-// per-expert exclusive prefix over chunks, then offsets over experts and the
-// tile schedule.  Pass 3: row = offset[e] + chunk base + rank.  Rows of an
-// expert come out in ascending token order; the result is unique.
+// One workgroup of 16 waves, all in LDS:
+//  1. per-expert token bitmap: bit t of bits[e] is set when token t chose e
+//     (each (token, slot) pair ORs one bit, so the bitmap is order-independent);
+//  2. per expert, an exclusive prefix of the popcounts of its 32-token words
+//     (one wave per expert, a wave-wide scan over the words);
+//  3. group offsets by a wave-wide scan over the groups, and the tile list:
+//     full 64-row tiles first, then partial tiles by descending height, so a
+//     launch that deals tiles in order starts the heaviest work first;
+//  4. row of (t, e) = offset[e] + prefix[e][t / 32] + popcount of the bits of
+//     bits[e][t / 32] below t.
+// Rows of an expert come out in ascending token order; the result is unique.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,7 +25,20 @@ namespace {
 
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
-constexpr int kMaxK = 16;
+constexpr int kMaxGroups = 257;
+
+// Exclusive wave-wide prefix sum (64 lanes), returns the lane's exclusive sum; *total = sum of all lanes.
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int lane = threadIdx.x % kWave;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  *total = __shfl(inc, kWave - 1, kWave);
+  return inc - v;
+}
 
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __restrict__ topk_ids,
                                                                int32_t* __restrict__ offsets,
@@ -29,112 +46,125 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
                                                                int32_t* __restrict__ token_row,
                                                                int32_t* __restrict__ sched, int T, int E, int k,
                                                                int S) {
-  extern __shared__ uint16_t cnt[];  // [chunks][E]: count, then exclusive base
-  __shared__ int32_t s_off[257 + 1];
-  __shared__ int32_t s_tile[257 + 1];
+  extern __shared__ uint32_t lds[];
+  const int W = (T + 31) / 32;                       // 32-token words per expert
+  uint32_t* bits = lds;                              // [E][W]
+  uint16_t* pre = (uint16_t*)(lds + (size_t)E * W);  // [E][W] exclusive popcount prefix
+  __shared__ int32_t s_off[kMaxGroups + 1];
+  __shared__ int32_t s_tile[kMaxGroups + 1];
+  __shared__ int32_t s_cnt[kMaxGroups];
   const int G = E + S;
-  const int chunks = (T + 63) / 64;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int kS = k + S;
-  for (int i = threadIdx.x; i < chunks * E; i += kPermThreads) cnt[i] = 0;
-  __syncthreads();
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int pairs = T * k;
 
-  // Pass 1: ballot ranks within each chunk.
-  for (int c = wave; c < chunks; c += kPermWaves) {
-    const int t = c * 64 + lane;
-    const bool valid = t < T;
-    int ids[kMaxK];
-    unsigned pending = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxK; ++j) {
-      int id = (valid && j < k) ? topk_ids[(size_t)t * k + j] : -1;
-      if ((unsigned)id < (unsigned)E) pending |= 1u << j;
-      else id = -1;
-      ids[j] = id;
+  for (int i = threadIdx.x; i < E * W; i += kPermThreads) bits[i] = 0u;
+  __syncthreads();
+  // 1. bitmap
+  for (int i = threadIdx.x; i < pairs; i += kPermThreads) {
+    const int e = topk_ids[i], t = i / k;
+    if ((unsigned)e < (unsigned)E) atomicOr(&bits[e * W + t / 32], 1u << (t % 32));
+  }
+  __syncthreads();
+  // 2. per-expert prefix over words
+  for (int e = wave; e < E; e += kPermWaves) {
+    int base = 0;
+    for (int w0 = 0; w0 < W; w0 += kWave) {
+      const int w = w0 + lane;
+      const int c = w < W ? __popc(bits[e * W + w]) : 0;
+      int tot;
+      const int ex = wave_excl_scan(c, &tot);
+      if (w < W) pre[e * W + w] = (uint16_t)(base + ex);
+      base += tot;
     }
-    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    while (true) {
-      const uint64_t act = __ballot(pending != 0);
-      if (act == 0) break;
-      const int leader = __ffsll((unsigned long long)act) - 1;
-      int cand = -1;
+    if (lane == 0) s_cnt[e] = base;
+  }
+  if (S && threadIdx.x == 0) s_cnt[E] = T;
+  __syncthreads();
+  // 3. offsets over groups (wave 0; each lane takes 5 consecutive groups), and
+  //    tile order: all full 64-row tiles first (by group), then the partial
+  //    tiles by descending height (ties by group) -- heavy tiles first.
+  __shared__ int32_t s_hist[kTileRows];  // partial tiles per height, then start slot per height
+  if (threadIdx.x < kTileRows) s_hist[threadIdx.x] = 0;
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int kPer = (kMaxGroups + kWave - 1) / kWave;
+    int rows_sum = 0, full_sum = 0;
 #pragma unroll
-      for (int j = kMaxK - 1; j >= 0; --j)
-        if ((pending >> j) & 1u) cand = ids[j];
-      const int e = __shfl(cand, leader, kWave);
-      int slot = -1;
+    for (int i = 0; i < kPer; ++i) {
+      const int g = lane * kPer + i;
+      const int n = g < G ? s_cnt[g] : 0;
+      rows_sum += n;
+      full_sum += n / kTileRows;
+    }
+    int rows_tot, full_tot;
+    int r = wave_excl_scan(rows_sum, &rows_tot);
+    int f = wave_excl_scan(full_sum, &full_tot);
 #pragma unroll
-      for (int j = kMaxK - 1; j >= 0; --j)
-        if (((pending >> j) & 1u) && ids[j] == e) slot = j;
-      const uint64_t m = __ballot(slot >= 0);
-      // A repeated expert id (not produced by the router) gets further ranks.
-      const int prev = cnt[c * E + e];
-      if (slot >= 0) {
-        token_row[(size_t)t * kS + slot] = prev + __popcll(m & below);  // rank, finalised in pass 3
-        pending &= ~(1u << slot);
+    for (int i = 0; i < kPer; ++i) {
+      const int g = lane * kPer + i;
+      if (g < G) {
+        const int n = s_cnt[g];
+        s_off[g] = r;
+        s_tile[g] = f;  // first full tile of g
+        r += n;
+        f += n / kTileRows;
+        if (n % kTileRows) atomicAdd(&s_hist[n % kTileRows], 1);
       }
-      if (lane == leader) cnt[c * E + e] = (uint16_t)(prev + __popcll(m));
+    }
+    if (lane == 0) {
+      s_off[G] = rows_tot;
+      s_tile[G] = full_tot;
     }
   }
   __syncthreads();
-
-  // Pass 2a: per-expert exclusive prefix over chunks.
-  for (int e = threadIdx.x; e < E; e += kPermThreads) {
-    int run = 0;
-    for (int c = 0; c < chunks; ++c) {
-      const int v = cnt[c * E + e];
-      cnt[c * E + e] = (uint16_t)run;
-      run += v;
+  if (threadIdx.x == 0) {  // start slot of each partial height, tallest first
+    int slot = s_tile[G];
+    for (int h = kTileRows - 1; h >= 1; --h) {
+      const int c = s_hist[h];
+      s_hist[h] = slot;
+      slot += c;
     }
-    s_tile[e] = run;  // total rows of expert e (temporarily)
+    s_hist[0] = slot;  // total tiles
   }
   __syncthreads();
-  // Pass 2b: offsets over groups and the tile schedule (one thread; G <= 257).
-  if (threadIdx.x == 0) {
-    int off = 0, tiles = 0;
-    for (int g = 0; g < G; ++g) {
-      const int n = (g < E) ? s_tile[g] : T;
-      s_off[g] = off;
-      s_tile[g] = tiles;
-      off += n;
-      tiles += (n + kTileRows - 1) / kTileRows;
-    }
-    s_off[G] = off;
-    s_tile[G] = tiles;
-    sched[0] = tiles;
-    sched[1] = G;
-    sched[2] = off;
-  }
   for (int i = threadIdx.x; i < kSchedHeader; i += kPermThreads)
-    if (i >= 3) sched[i] = 0;
-  __syncthreads();
+    sched[i] = i == 0 ? s_hist[0] : i == 1 ? G : i == 2 ? s_off[G] : 0;
   for (int g = threadIdx.x; g <= G; g += kPermThreads) offsets[g] = s_off[g];
   for (int g = threadIdx.x; g < G; g += kPermThreads) {
     const int n = s_off[g + 1] - s_off[g];
+    const int full = n / kTileRows, rem = n % kTileRows;
     int32_t* dst = sched + kSchedHeader + (size_t)s_tile[g] * kTileInts;
-    for (int i = 0; i * kTileRows < n; ++i) {
+    for (int i = 0; i < full; ++i) {
       dst[i * kTileInts + 0] = g;
       dst[i * kTileInts + 1] = s_off[g] + i * kTileRows;
-      dst[i * kTileInts + 2] = min(kTileRows, n - i * kTileRows);
+      dst[i * kTileInts + 2] = kTileRows;
       dst[i * kTileInts + 3] = 0;
     }
+    if (rem) {
+      // rank among partial tiles of the same height: groups below g with that height
+      int before = 0;
+      for (int h = 0; h < g; ++h) before += ((s_off[h + 1] - s_off[h]) % kTileRows) == rem;
+      int32_t* t = sched + kSchedHeader + (size_t)(s_hist[rem] + before) * kTileInts;
+      t[0] = g;
+      t[1] = s_off[g] + full * kTileRows;
+      t[2] = rem;
+      t[3] = 0;
+    }
   }
-
-  // Pass 3: final rows.
-  for (int c = wave; c < chunks; c += kPermWaves) {
-    const int t = c * 64 + lane;
-    if (t >= T) continue;
-    for (int j = 0; j < k; ++j) {
-      const int e = topk_ids[(size_t)t * k + j];
-      if ((unsigned)e >= (unsigned)E) {  // not produced by the router: no row
-        token_row[(size_t)t * kS + j] = -1;
-        continue;
-      }
-      const int row = s_off[e] + cnt[c * E + e] + token_row[(size_t)t * kS + j];
-      token_row[(size_t)t * kS + j] = row;
+  // 4. rows
+  for (int i = threadIdx.x; i < pairs; i += kPermThreads) {
+    const int e = topk_ids[i], t = i / k, j = i % k;
+    int row = -1;
+    if ((unsigned)e < (unsigned)E) {
+      const int w = e * W + t / 32;
+      row = s_off[e] + pre[w] + __popc(bits[w] & ((1u << (t % 32)) - 1u));
       row_token[row] = t;
     }
-    if (S) {
+    token_row[(size_t)t * kS + j] = row;
+  }
+  if (S) {
+    for (int t = threadIdx.x; t < T; t += kPermThreads) {
       const int row = s_off[E] + t;
       token_row[(size_t)t * kS + k] = row;
       row_token[row] = t;
@@ -171,7 +201,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 }  // namespace
 
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
-  const size_t lds = (size_t)((a.T + 63) / 64) * a.E * sizeof(uint16_t);
+  const size_t lds = permute_lds_bytes(a.T, a.E);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, stream, a.topk_ids, a.offsets, a.row_token,
                      a.token_row, a.sched, a.T, a.E, a.k, a.S);
   return hipGetLastError();

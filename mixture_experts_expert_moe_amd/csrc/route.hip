@@ -15,7 +15,7 @@
 namespace moe {
 namespace {
 
-constexpr int kRouteWaves = 4;  // waves per block; each takes a quarter of H
+constexpr int kRouteWaves = 8;  // waves per block; each takes an eighth of H
 
 // One block computes logits for 16 tokens x 16 experts.  Lane l of a wave
 // holds token/expert (l % 16) and loads 8 consecutive h (one 16-byte load for
@@ -34,47 +34,67 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
   const int t = min(t0 + r, T - 1), e = min(e0 + r, E - 1);
   const int hq = H / kRouteWaves;
   const int hbeg = wave * hq;
-  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
-  for (int h = hbeg; h < hbeg + hq; h += 32) {
-    const int hh = h + 8 * q;
-    float xa[8], wb[8];
-    if constexpr (kF32) {
-      const float* xp = (const float*)x + (size_t)t * H + hh;
-      const float* wp = (const float*)wr + (size_t)e * H + hh;
-      const u32x4 x0 = ld16(xp), x1 = ld16(xp + 4), w0 = ld16(wp), w1 = ld16(wp + 4);
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};  // two independent MFMA chains
+  // Batches of 8 steps of 32 h: all loads of a batch are issued before its MFMAs.
+  constexpr int kNb = 8;
+  for (int h0 = hbeg; h0 < hbeg + hq; h0 += 32 * kNb) {
+    u32x4 xv[kNb][kF32 ? 2 : 1], wv[kNb][kF32 ? 2 : 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[i] = __uint_as_float(x0[i]);
-        xa[4 + i] = __uint_as_float(x1[i]);
-        wb[i] = __uint_as_float(w0[i]);
-        wb[4 + i] = __uint_as_float(w1[i]);
-      }
-    } else {
-      const u32x4 xv = ld16((const uint16_t*)x + (size_t)t * H + hh);
-      const u32x4 wv = ld16((const uint16_t*)wr + (size_t)e * H + hh);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        xa[2 * i] = __uint_as_float(xv[i] << 16);
-        xa[2 * i + 1] = __uint_as_float(xv[i] & 0xffff0000u);
-        wb[2 * i] = __uint_as_float(wv[i] << 16);
-        wb[2 * i + 1] = __uint_as_float(wv[i] & 0xffff0000u);
+    for (int u = 0; u < kNb; ++u) {
+      const int hh = h0 + 32 * u + 8 * q;
+      if (h0 + 32 * u < hbeg + hq) {
+        if constexpr (kF32) {
+          const float* xp = (const float*)x + (size_t)t * H + hh;
+          const float* wp = (const float*)wr + (size_t)e * H + hh;
+          xv[u][0] = ld16(xp);
+          xv[u][1] = ld16(xp + 4);
+          wv[u][0] = ld16(wp);
+          wv[u][1] = ld16(wp + 4);
+        } else {
+          xv[u][0] = ld16((const uint16_t*)x + (size_t)t * H + hh);
+          wv[u][0] = ld16((const uint16_t*)wr + (size_t)e * H + hh);
+        }
       }
     }
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[s], (double)wb[s], acc, 0, 0, 0);
+    for (int u = 0; u < kNb; ++u) {
+      if (h0 + 32 * u < hbeg + hq) {
+        float xa[8], wb[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (kF32) {
+            xa[i] = __uint_as_float(xv[u][0][i]);
+            xa[4 + i] = __uint_as_float(xv[u][1][i]);
+            wb[i] = __uint_as_float(wv[u][0][i]);
+            wb[4 + i] = __uint_as_float(wv[u][1][i]);
+          } else {
+            xa[2 * i] = __uint_as_float(xv[u][0][i] << 16);
+            xa[2 * i + 1] = __uint_as_float(xv[u][0][i] & 0xffff0000u);
+            wb[2 * i] = __uint_as_float(wv[u][0][i] << 16);
+            wb[2 * i + 1] = __uint_as_float(wv[u][0][i] & 0xffff0000u);
+          }
+        }
+#pragma unroll
+        for (int s = 0; s < 8; s += 2) {
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[s], (double)wb[s], acc, 0, 0, 0);
+          acc2 = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xa[s + 1], (double)wb[s + 1], acc2, 0, 0, 0);
+        }
+      }
+    }
   }
   // D layout of the f64 16x16x4 MFMA: lane l, register i holds D[4 * i + l / 16][l % 16]
   // (row = token, column = expert) -- unlike the f32-output MFMAs, whose register i
   // holds row 4 * (l / 16) + i.
 #pragma unroll
-  for (int i = 0; i < 4; ++i) part[wave][4 * i + q][r] = acc[i];
+  for (int i = 0; i < 4; ++i) part[wave][4 * i + q][r] = acc[i] + acc2[i];
   __syncthreads();
   if (wave == 0) {
     for (int idx = lane; idx < 256; idx += kWave) {
       const int tt = idx / 16, ee = idx % 16;
       if (t0 + tt < T && e0 + ee < E) {
-        const double s = ((part[0][tt][ee] + part[1][tt][ee]) + part[2][tt][ee]) + part[3][tt][ee];
+        double s = part[0][tt][ee];
+#pragma unroll
+        for (int w = 1; w < kRouteWaves; ++w) s += part[w][tt][ee];
         float v = (float)s;
         if (bias) v = __fadd_rn(v, bias[e0 + ee]);
         logits[(size_t)(t0 + tt) * E + e0 + ee] = v;

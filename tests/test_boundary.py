@@ -67,9 +67,9 @@ def test_buffer_sizes_match_shapes():
 @pytest.mark.parametrize("kw,code", [
     (dict(hidden=2000), -2), (dict(inter=300), -2), (dict(top_k=0), -1), (dict(top_k=129), -1),
     (dict(top_k=17, n_routed=32), -2), (dict(n_shared=2), -1), (dict(max_tokens=0), -1),
-    (dict(max_tokens=20000), -2), (dict(n_routed=257, top_k=8), -2), (dict(act="f32", wt="bf16"), -2),
+    (dict(max_tokens=2600), -2), (dict(n_routed=257, top_k=8), -2), (dict(act="f32", wt="bf16"), -2),
     (dict(act="bf16", wt="f32"), -2), (dict(out="i8"), -2), (dict(act="i8"), -2),
-    (dict(n_routed=256, max_tokens=16384), -2),
+    (dict(n_routed=256, max_tokens=1300), -2),
 ])
 def test_bad_desc_rejected(kw, code):
     sizes = (ctypes.c_size_t * 13)()
