@@ -194,6 +194,7 @@ def main():
     ap.add_argument("--rotations", type=int, default=4, help="distinct weight sets cycled per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the int8 T=8 decode figure")
+    ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit T=2048 prefill figure")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a reference kernel of known "
@@ -261,6 +262,26 @@ def main():
             "gemm_algorithmic_bytes": b,
         }
         del rd
+        torch.cuda.empty_cache()
+
+    if not args.no_q4:
+        Tq = 2048
+        rq = Runner("q4_e128_top8_shared_zipf", Tq, max(args.rotations, 4), min(args.steps + args.warmup, 24))
+        stq = max(3, min(args.steps, 12))
+        wq, Uq, kq = rq.timed(stq, min(args.warmup, 3))
+        msq = wq / stq * 1e3
+        Rq = Tq * (rq.spec.top_k + rq.spec.n_shared)
+        fl_gu = 2.0 * Rq * 2 * rq.spec.inter * rq.spec.hidden
+        fl_dn = 2.0 * Rq * rq.spec.hidden * rq.spec.inter
+        extra["prefill_q4_zipf_t2048"] = {
+            "tokens_per_s": round(Tq / (msq / 1e3), 1), "ms_per_step": round(msq, 5),
+            "kernel_ms": {k: round(v, 5) for k, v in kq.items()}, "touched_groups": Uq,
+            "gate_up_mfma_frac": round(fl_gu / (kq["gate_up"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "down_mfma_frac": round(fl_dn / (kq["down"] / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "gemm_mfma_frac": round((fl_gu + fl_dn) / ((kq["gate_up"] + kq["down"]) / 1e3) / 1e12
+                                    / MFMA_BF16_PEAK_TFLOPS, 4),
+        }
+        del rq
         torch.cuda.empty_cache()
 
     line = {

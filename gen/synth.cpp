@@ -32,6 +32,9 @@ inline uint64_t mix64(uint64_t z) {
 
 inline uint64_t draw(uint64_t key, uint64_t i) { return mix64(key + (i + 1) * kGamma); }
 
+// Key of sub-stream b of stream a (also exported as synth_mix).
+inline uint64_t stream_key(uint64_t a, uint64_t b) { return mix64(mix64(a) ^ (b * kGamma + 0x5EED2026ULL)); }
+
 // Uniform in (0, 1]: top 53 bits, offset by one so log() is finite.
 inline double unit_open0(uint64_t r) { return (double)((r >> 11) + 1) * (1.0 / 9007199254740992.0); }
 
@@ -105,23 +108,54 @@ inline float value(uint64_t key, int64_t i, float mean, float std_) {
   return (float)((double)mean + (double)std_ * normal_at(key, (uint64_t)i));
 }
 
+// Elements [i0, i0 + n) of a stream, each Box-Muller pair computed once
+// (the same values as value() element by element).
+inline void fill_values(uint64_t key, int64_t i0, int64_t n, float mean, float std_, float* out) {
+  int64_t i = i0, end = i0 + n;
+  if (i < end && (i & 1)) { *out++ = value(key, i, mean, std_); ++i; }
+  for (; i + 1 < end; i += 2) {
+    const uint64_t p = (uint64_t)i >> 1;
+    const double u1 = unit_open0(draw(key, 2 * p));
+    const double u2 = unit_open0(draw(key, 2 * p + 1));
+    const double r = std::sqrt(-2.0 * std::log(u1));
+    const double a = 6.283185307179586476925286766559 * u2;
+    *out++ = (float)((double)mean + (double)std_ * (r * std::cos(a)));
+    *out++ = (float)((double)mean + (double)std_ * (r * std::sin(a)));
+  }
+  if (i < end) *out++ = value(key, i, mean, std_);
+}
+
+// Rows [lo, hi) of the G*n rows, each row k values of matrix g = row / n.
+template <class Store>
+void weight_rows(uint64_t key, int32_t n, int32_t k, float std_, int64_t lo, int64_t hi, Store store) {
+  std::vector<float> w((size_t)k);
+  for (int64_t r = lo; r < hi; ++r) {
+    const int64_t g = r / n, row = r % n;
+    fill_values(stream_key(key, (uint64_t)g), row * (int64_t)k, k, 0.f, std_, w.data());
+    store(r, w.data());
+  }
+}
+
 }  // namespace
 
 extern "C" {
 
-uint64_t synth_mix(uint64_t a, uint64_t b) { return mix64(mix64(a) ^ (b * kGamma + 0x5EED2026ULL)); }
+uint64_t synth_mix(uint64_t a, uint64_t b) { return stream_key(a, b); }
 
 // n draws of N(mean, std), stored as fp32.
 void synth_normal_f32(uint64_t key, int64_t n, float mean, float std_, float* out, int threads) {
-  parallel_for(n, threads, [&](int64_t lo, int64_t hi) {
-    for (int64_t i = lo; i < hi; ++i) out[i] = value(key, i, mean, std_);
-  });
+  parallel_for(n, threads, [&](int64_t lo, int64_t hi) { fill_values(key, lo, hi - lo, mean, std_, out + lo); });
 }
 
 // n draws of N(mean, std), stored as bf16 bits (fp32 value rounded to nearest even).
 void synth_normal_bf16(uint64_t key, int64_t n, float mean, float std_, uint16_t* out, int threads) {
   parallel_for(n, threads, [&](int64_t lo, int64_t hi) {
-    for (int64_t i = lo; i < hi; ++i) out[i] = to_bf16(value(key, i, mean, std_));
+    std::vector<float> buf(4096);
+    for (int64_t i = lo; i < hi; i += 4096) {
+      const int64_t m = std::min<int64_t>(4096, hi - i);
+      fill_values(key, i, m, mean, std_, buf.data());
+      for (int64_t j = 0; j < m; ++j) out[i + j] = to_bf16(buf[j]);
+    }
   });
 }
 
@@ -138,10 +172,8 @@ void synth_weights_i8(uint64_t key, int32_t G, int32_t n, int32_t k, float std_,
       const int64_t g = r / n, row = r % n;
       const uint64_t kg = synth_mix(key, (uint64_t)g);
       float amax = 0.f;
-      for (int32_t c = 0; c < k; ++c) {
-        w[c] = value(kg, row * (int64_t)k + c, 0.f, std_);
-        amax = std::max(amax, std::fabs(w[c]));
-      }
+      fill_values(kg, row * (int64_t)k, k, 0.f, std_, w.data());
+      for (int32_t c = 0; c < k; ++c) amax = std::max(amax, std::fabs(w[c]));
       const float s = amax / 127.0f;
       scale[r] = s;
       for (int32_t c = 0; c < k; ++c) {
@@ -169,8 +201,8 @@ void synth_weights_q4(uint64_t key, int32_t G, int32_t n, int32_t k, float std_,
       for (int32_t b = 0; b < nb; ++b) {
         float w[32];
         float mn = INFINITY, mx = -INFINITY;
+        fill_values(kg, row * (int64_t)k + b * 32, 32, 0.f, std_, w);
         for (int j = 0; j < 32; ++j) {
-          w[j] = value(kg, row * (int64_t)k + b * 32 + j, 0.f, std_);
           mn = std::min(mn, w[j]);
           mx = std::max(mx, w[j]);
         }
@@ -195,16 +227,18 @@ void synth_weights_q4(uint64_t key, int32_t G, int32_t n, int32_t k, float std_,
 
 // G matrices [n][k] of N(0, std) as fp32 or bf16 (matrix g uses key synth_mix(key, g)).
 void synth_weights_f32(uint64_t key, int32_t G, int32_t n, int32_t k, float std_, float* out, int threads) {
-  const int64_t per = (int64_t)n * k;
-  parallel_for((int64_t)G * per, threads, [&](int64_t lo, int64_t hi) {
-    for (int64_t i = lo; i < hi; ++i) out[i] = value(synth_mix(key, (uint64_t)(i / per)), i % per, 0.f, std_);
+  parallel_for((int64_t)G * n, threads, [&](int64_t lo, int64_t hi) {
+    weight_rows(key, n, k, std_, lo, hi, [&](int64_t r, const float* w) {
+      std::memcpy(out + r * (int64_t)k, w, sizeof(float) * (size_t)k);
+    });
   });
 }
 
 void synth_weights_bf16(uint64_t key, int32_t G, int32_t n, int32_t k, float std_, uint16_t* out, int threads) {
-  const int64_t per = (int64_t)n * k;
-  parallel_for((int64_t)G * per, threads, [&](int64_t lo, int64_t hi) {
-    for (int64_t i = lo; i < hi; ++i) out[i] = to_bf16(value(synth_mix(key, (uint64_t)(i / per)), i % per, 0.f, std_));
+  parallel_for((int64_t)G * n, threads, [&](int64_t lo, int64_t hi) {
+    weight_rows(key, n, k, std_, lo, hi, [&](int64_t r, const float* w) {
+      for (int32_t c = 0; c < k; ++c) out[r * (int64_t)k + c] = to_bf16(w[c]);
+    });
   });
 }
 

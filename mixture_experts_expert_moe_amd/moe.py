@@ -189,3 +189,44 @@ class MoeLayer:
         t = self.tensors[name]
         n = math.prod(shape)
         return t.view(dtype)[:n].view(*shape)
+
+
+class MoeStack:
+    """Layers of `MoeLayer` with RMSNorm before each and an fp32 residual stream:
+    x_{l+1} = x_l + MoE_l(RMSNorm(x_l)).  One shared set of buffers; per-layer
+    weights.  x is [T][H] fp32 on the device and is updated in place (ping-pong
+    through a second buffer)."""
+
+    def __init__(self, desc: MoeDesc, layer_weights: list, eps: float = 1e-6, device="cuda"):
+        import torch
+        self.desc = desc
+        self.eps = eps
+        self.layers = layer_weights
+        self.tensors, self.bufs = alloc_buffers(desc, device)
+        self.gu = [weights_struct(w["w_gu"], w.get("w_gu_scale"), w.get("w_gu_min")) for w in layer_weights]
+        self.dn = [weights_struct(w["w_down"], w.get("w_down_scale"), w.get("w_down_min")) for w in layer_weights]
+        M, H = desc.max_tokens, desc.hidden
+        self.xn = torch.empty((M, H), dtype=torch.bfloat16, device=device)
+        self.tmp = torch.empty((M, H), dtype=torch.float32, device=device)
+
+    def layer(self, l, x, out, T, stream=None):
+        """One layer on the first T rows: out = x + MoE_l(RMSNorm(x))."""
+        d, b, w = self.desc, self.bufs, self.layers[l]
+        xn = self.xn[:T]
+        moe_rmsnorm(T, d.hidden, self.eps, x, xn, stream)
+        moe_route_topk(d, T, xn, w["w_router"], w.get("bias"), b, stream)
+        moe_permute(d, T, xn, b, stream)
+        moe_grouped_gemm_gu(d, T, xn, self.gu[l], b, stream)
+        moe_grouped_gemm_down(d, T, self.dn[l], b, stream)
+        moe_combine(d, T, x, out, b, stream)
+
+    def forward(self, x, stream=None):
+        """All layers on x ([T][H] fp32, T <= max_tokens); returns the tensor holding the result."""
+        T = x.shape[0]
+        a, b = x, self.tmp[:T]
+        for l in range(len(self.layers)):
+            self.layer(l, a, b, T, stream)
+            a, b = b, a
+        if a.data_ptr() != x.data_ptr():
+            x.copy_(a)
+        return x
