@@ -186,6 +186,76 @@ def cpu_baseline(name, T, sample_tokens, batches=3):
                       % (batches, sample_tokens, T, name, dt, threads)}
 
 
+def stack_figures():
+    """40 stacked 4-bit layers (RMSNorm + residual): a 2600-token prompt in
+    256-token chunks, then 64 single-token decode steps, eager and replayed
+    from one captured HIP graph per step."""
+    import torch
+    from gen import synth
+    from mixture_experts_expert_moe_amd import moe
+    from tests import gpu_harness as gh
+    name = "q4_stack40"
+    wl = synth.workload(name)
+    spec, L, ex = wl.spec, wl.layers, wl.extra
+    wid = synth.workload_id(name)
+    t0 = time.time()
+    dev = [gh.dev_weights(synth.layer_weights(spec, wid, l)) for l in range(L)]
+    x0 = torch.from_numpy(synth.tokens(spec, wid, ex["prompt"], stream=0, dtype="f32")).to("cuda")
+    dec = torch.from_numpy(np.concatenate([synth.tokens(spec, wid, 1, stream=1 + s, dtype="f32")
+                                           for s in range(ex["decode_steps"])])).to("cuda")
+    log("[bench] %s: %d layers generated and uploaded in %.1f s" % (name, L, time.time() - t0))
+    st = moe.MoeStack(gh.desc_for(spec, ex["chunk"]), dev, eps=ex["eps"])
+    P, C = ex["prompt"], ex["chunk"]
+
+    def prefill():
+        x = x0.clone()
+        for c0 in range(0, P, C):
+            st.forward(x[c0:c0 + C])  # row slices are contiguous; updated in place
+        return x
+
+    prefill()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    prefill()
+    torch.cuda.synchronize()
+    t_pre = time.perf_counter() - t
+    xs = dec.clone()
+    for s in range(4):
+        st.forward(xs[s:s + 1])
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for s in range(dec.shape[0]):
+        st.forward(xs[s:s + 1])
+    torch.cuda.synchronize()
+    t_dec = time.perf_counter() - t
+    # one decode step (40 layers) captured as a graph, replayed per token
+    buf = torch.empty((1, spec.hidden), dtype=torch.float32, device="cuda")
+    buf.copy_(dec[0:1])
+    st.forward(buf)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        st.forward(buf)
+    for s in range(4):
+        g.replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for s in range(dec.shape[0]):
+        buf.copy_(dec[s:s + 1])
+        g.replay()
+    torch.cuda.synchronize()
+    t_graph = time.perf_counter() - t
+    weights = L * spec.groups * (weight_bytes(spec, 2 * spec.inter, spec.hidden) + weight_bytes(spec, spec.hidden,
+                                                                                               spec.inter))
+    out = {"prefill_tokens_per_s": round(P / t_pre, 1), "prefill_ms": round(t_pre * 1e3, 3),
+           "decode_tokens_per_s": round(dec.shape[0] / t_dec, 1),
+           "decode_graph_tokens_per_s": round(dec.shape[0] / t_graph, 1),
+           "decode_graph_ms_per_token": round(t_graph / dec.shape[0] * 1e3, 4),
+           "layers": L, "weight_bytes_all_layers": weights}
+    del st, dev
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,6 +265,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the int8 T=8 decode figure")
     ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit T=2048 prefill figure")
+    ap.add_argument("--no-fp32", action="store_true", help="skip the fp32 16-expert figure")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer 4-bit stack figures")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a reference kernel of known "
@@ -250,20 +322,33 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_decode:
-        Td = 8
-        rd = Runner("int8_e128_top8_shared", Td, max(args.rotations, 4), args.steps + args.warmup)
-        wd, Ud, kd = rd.timed(args.steps, args.warmup)
-        msd = wd / args.steps * 1e3
-        b = gu_algorithmic_bytes(rd.spec, Td, Ud) + down_algorithmic_bytes(rd.spec, Td, Ud)
-        extra["decode_int8_t8"] = {
-            "tokens_per_s": round(Td / (msd / 1e3), 1), "ms_per_step": round(msd, 5),
-            "kernel_ms": {k: round(v, 5) for k, v in kd.items()}, "touched_groups": Ud,
-            "gemm_hbm_frac": round(b / ((kd["gate_up"] + kd["down"]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "gemm_algorithmic_bytes": b,
-        }
-        del rd
+        sweep = {}
+        for Td in (1, 2, 4, 8):
+            rd = Runner("int8_e128_top8_shared", Td, max(args.rotations, 4), args.steps + args.warmup)
+            wd, Ud, kd = rd.timed(args.steps, args.warmup)
+            msd = wd / args.steps * 1e3
+            b = gu_algorithmic_bytes(rd.spec, Td, Ud) + down_algorithmic_bytes(rd.spec, Td, Ud)
+            sweep[Td] = {
+                "tokens_per_s": round(Td / (msd / 1e3), 1), "ms_per_step": round(msd, 5),
+                "kernel_ms": {k: round(v, 5) for k, v in kd.items()}, "touched_groups": Ud,
+                "gemm_hbm_frac": round(b / ((kd["gate_up"] + kd["down"]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+                "gemm_algorithmic_bytes": b,
+            }
+            del rd
+            torch.cuda.empty_cache()
+        extra["decode_int8_t8"] = sweep[8]
+        extra["decode_int8_sweep"] = {str(t): {k: v for k, v in r.items() if k != "kernel_ms"} for t, r in sweep.items()}
+    if not args.no_fp32:
+        r1 = Runner("fp32_e16_top2", 16, max(args.rotations, 4), args.steps + args.warmup)
+        w1, U1, k1 = r1.timed(args.steps, args.warmup)
+        ms1 = w1 / args.steps * 1e3
+        b1 = gu_algorithmic_bytes(r1.spec, 16, U1) + down_algorithmic_bytes(r1.spec, 16, U1)
+        extra["fp32_e16_top2_t16"] = {
+            "tokens_per_s": round(16 / (ms1 / 1e3), 1), "ms_per_step": round(ms1, 5), "touched_groups": U1,
+            "kernel_ms": {k: round(v, 5) for k, v in k1.items()},
+            "gemm_hbm_frac": round(b1 / ((k1["gate_up"] + k1["down"]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del r1
         torch.cuda.empty_cache()
-
     if not args.no_q4:
         Tq = 2048
         rq = Runner("q4_e128_top8_shared_zipf", Tq, max(args.rotations, 4), min(args.steps + args.warmup, 24))
@@ -282,6 +367,10 @@ def main():
                                     / MFMA_BF16_PEAK_TFLOPS, 4),
         }
         del rq
+        torch.cuda.empty_cache()
+
+    if not args.no_stack:
+        extra["stack40_q4"] = stack_figures()
         torch.cuda.empty_cache()
 
     line = {
