@@ -16,7 +16,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_gfx950.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "permute.hip", "gemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_big.hip", "combine.hip", "moe_api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

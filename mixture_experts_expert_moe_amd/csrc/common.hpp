@@ -17,11 +17,16 @@ typedef __attribute__((ext_vector_type(4))) double f64x4;
 constexpr int kWave = 64;
 
 // Layout of the tile schedule written by moe_permute (int32):
-//   [0] number of tiles, [1] groups, [2] rows, [3..31] zero (reserved),
-//   then {group, row0, rows, 0} per tile from index kSchedHeader.
+//   [0] number of small tiles, [1] groups, [2] rows, [3] number of big tiles,
+//   [4] index of the first big tile, [5..31] zero (reserved);
+//   small tiles {group, row0, rows, 0} from index kSchedHeader, big tiles from [4].
 constexpr int kSchedHeader = 32;
+constexpr int kSchedSmall = 0, kSchedGroups = 1, kSchedRows = 2, kSchedBig = 3, kSchedBigStart = 4;
 constexpr int kTileInts = 4;
-constexpr int kTileRows = 64;     // at most 64 rows of one group per tile
+constexpr int kTileRows = 64;       // at most 64 rows of one group per small tile
+constexpr int kBigTileRows = 256;   // rows per big tile
+constexpr int kBigTileMin = 128;    // a group needs at least this many rows for big tiles
+constexpr int kBigTileMinTokens = 1024;  // big tiles are used for calls with T >= this
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }

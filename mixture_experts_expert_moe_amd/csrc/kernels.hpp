@@ -27,6 +27,8 @@ struct PermuteArgs {
   int32_t* token_row;
   int32_t* sched;
   int T, E, k, S;
+  bool big_on;    // cut groups of >= 128 rows into 256-row big tiles
+  int big_start;  // int index of the big-tile list in the schedule
 };
 
 struct QuantArgs {  // per-row symmetric int8 quantisation
@@ -52,6 +54,7 @@ struct GemmArgs {
   int K;                    // reduction length (H for gate/up, I for down)
   int N;                    // output columns (I for gate/up, H for down)
   int wfmt;                 // WFmt (also fixes the activation/output formats, see moe.h)
+  bool big_on;              // the schedule has big tiles (launch the big-tile kernel too)
   int T;                    // tokens (gate/up clamps row_token into [0, T))
   int R;                    // permuted rows, T * (k + S)
   int G;                    // groups
@@ -73,6 +76,8 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_gate_up(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_down(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_big_down(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, uint16_t* xn, int T, int H, float eps, hipStream_t stream);
 
@@ -81,7 +86,10 @@ hipError_t launch_rmsnorm(const float* x, uint16_t* xn, int T, int H, float eps,
 inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)((T + 31) / 32) * (size_t)E * 6; }
 constexpr size_t kPermuteMaxLds = 60 * 1024;
 
-// Capacity of the tile schedule (ints) for R_max rows over G groups.
-inline size_t sched_ints(int64_t r_max, int64_t G) { return 32 + 4 * (size_t)((r_max + 63) / 64 + G); }
+// Tile schedule capacity for R_max rows over G groups: small tiles first,
+// then the big-tile list (at most one big tile per 128 rows).
+inline size_t sched_small_cap(int64_t r_max, int64_t G) { return (size_t)((r_max + 63) / 64 + G); }
+inline size_t sched_big_start(int64_t r_max, int64_t G) { return 32 + 4 * sched_small_cap(r_max, G); }
+inline size_t sched_ints(int64_t r_max, int64_t G) { return sched_big_start(r_max, G) + 4 * (size_t)(r_max / 128 + 1); }
 
 }  // namespace moe

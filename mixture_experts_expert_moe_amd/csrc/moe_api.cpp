@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include "common.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -55,6 +56,12 @@ int64_t rows(const moe_desc* d, int64_t T) { return T * (d->top_k + d->n_shared)
 bool f32_intermediates(const moe_desc* d) { return d->w_dtype == MOE_F32 || d->w_dtype == MOE_I8; }
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Big tiles (256 rows, LDS-staged, compute-bound kernel) for long prefill
+// chunks with bf16 or 4-bit weights; a host-side rule on T alone.
+bool big_tiles(const moe_desc* d, int32_t T) {
+  return T >= moe::kBigTileMinTokens && (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_Q4B32);
+}
 
 moe_status check_weights(const moe_desc* d, const moe_weights* w) {
   if (!w || !ptr_ok(w->w)) return MOE_ERR_INVALID_ARG;
@@ -131,8 +138,9 @@ moe_status moe_permute(const moe_desc* d, int32_t T, const void* x, const moe_bu
     const hipError_t e = moe::launch_quant_rows(q, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
+  const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
   moe::PermuteArgs a{b->topk_ids, b->expert_offsets, b->row_token, b->token_row, b->sched, T, d->n_routed,
-                     d->top_k, d->n_shared};
+                     d->top_k, d->n_shared, big_tiles(d, T), (int)moe::sched_big_start(r_max, groups(d))};
   return hip_status(moe::launch_permute(a, stream));
 }
 
@@ -161,6 +169,11 @@ moe_status moe_grouped_gemm_gu(const moe_desc* d, int32_t T, const void* x, cons
   a.T = T;
   a.R = (int)rows(d, T);
   a.G = groups(d);
+  a.big_on = big_tiles(d, T);
+  if (a.big_on) {
+    const hipError_t e = moe::launch_big_gate_up(a, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   return hip_status(moe::launch_gate_up(a, stream));
 }
 
@@ -195,6 +208,11 @@ moe_status moe_grouped_gemm_down(const moe_desc* d, int32_t T, const moe_weights
   a.T = T;
   a.R = R;
   a.G = groups(d);
+  a.big_on = big_tiles(d, T);
+  if (a.big_on) {
+    const hipError_t e = moe::launch_big_down(a, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   return hip_status(moe::launch_down(a, stream));
 }
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
                                                                int32_t* __restrict__ row_token,
                                                                int32_t* __restrict__ token_row,
                                                                int32_t* __restrict__ sched, int T, int E, int k,
-                                                               int S) {
+                                                               int S, int big_on, int big_start) {
   extern __shared__ uint32_t lds[];
   const int W = (T + 31) / 32;                       // 32-token words per expert
   uint32_t* bits = lds;                              // [E][W]
@@ -81,40 +81,61 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   }
   if (S && threadIdx.x == 0) s_cnt[E] = T;
   __syncthreads();
-  // 3. offsets over groups (wave 0; each lane takes 5 consecutive groups), and
-  //    tile order: all full 64-row tiles first (by group), then the partial
-  //    tiles by descending height (ties by group) -- heavy tiles first.
-  __shared__ int32_t s_hist[kTileRows];  // partial tiles per height, then start slot per height
+  // 3. offsets over groups, then the two tile lists (wave 0 scans; each lane
+  //    takes 5 consecutive groups).  With big tiles on, a group of >= 128 rows
+  //    is cut into tiles of 256 rows (a remainder of >= 128 rows is one more,
+  //    partial, big tile; a smaller remainder goes to small tiles).  Small
+  //    tiles hold <= 64 rows: all full ones first (by group), then the partial
+  //    ones by descending height (ties by group) -- heavy tiles first.
+  __shared__ int32_t s_hist[kTileRows];  // partial small tiles per height, then start slot per height
+  __shared__ int32_t s_small[kMaxGroups];      // rows of g handled by small tiles (the last rows of g)
+  __shared__ int32_t s_big[kMaxGroups + 1];    // first big tile of g
   if (threadIdx.x < kTileRows) s_hist[threadIdx.x] = 0;
   __syncthreads();
   if (wave == 0) {
     constexpr int kPer = (kMaxGroups + kWave - 1) / kWave;
-    int rows_sum = 0, full_sum = 0;
+    int rows_sum = 0, full_sum = 0, big_sum = 0;
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int g = lane * kPer + i;
       const int n = g < G ? s_cnt[g] : 0;
+      int nbig = 0, nsmall = n;
+      if (big_on && n >= kBigTileMin) {
+        nbig = n / kBigTileRows + (n % kBigTileRows >= kBigTileMin ? 1 : 0);
+        nsmall = n % kBigTileRows >= kBigTileMin ? 0 : n % kBigTileRows;
+      }
       rows_sum += n;
-      full_sum += n / kTileRows;
+      full_sum += nsmall / kTileRows;
+      big_sum += nbig;
     }
-    int rows_tot, full_tot;
+    int rows_tot, full_tot, big_tot;
     int r = wave_excl_scan(rows_sum, &rows_tot);
     int f = wave_excl_scan(full_sum, &full_tot);
+    int b = wave_excl_scan(big_sum, &big_tot);
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int g = lane * kPer + i;
       if (g < G) {
         const int n = s_cnt[g];
+        int nbig = 0, nsmall = n;
+        if (big_on && n >= kBigTileMin) {
+          nbig = n / kBigTileRows + (n % kBigTileRows >= kBigTileMin ? 1 : 0);
+          nsmall = n % kBigTileRows >= kBigTileMin ? 0 : n % kBigTileRows;
+        }
         s_off[g] = r;
-        s_tile[g] = f;  // first full tile of g
+        s_tile[g] = f;  // first full small tile of g
+        s_big[g] = b;
+        s_small[g] = nsmall;
         r += n;
-        f += n / kTileRows;
-        if (n % kTileRows) atomicAdd(&s_hist[n % kTileRows], 1);
+        f += nsmall / kTileRows;
+        b += nbig;
+        if (nsmall % kTileRows) atomicAdd(&s_hist[nsmall % kTileRows], 1);
       }
     }
     if (lane == 0) {
       s_off[G] = rows_tot;
       s_tile[G] = full_tot;
+      s_big[G] = big_tot;
     }
   }
   __syncthreads();
@@ -125,29 +146,42 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
       s_hist[h] = slot;
       slot += c;
     }
-    s_hist[0] = slot;  // total tiles
+    s_hist[0] = slot;  // total small tiles
   }
   __syncthreads();
   for (int i = threadIdx.x; i < kSchedHeader; i += kPermThreads)
-    sched[i] = i == 0 ? s_hist[0] : i == 1 ? G : i == 2 ? s_off[G] : 0;
+    sched[i] = i == kSchedSmall ? s_hist[0] : i == kSchedGroups ? G : i == kSchedRows ? s_off[G]
+             : i == kSchedBig ? s_big[G] : i == kSchedBigStart ? big_start : 0;
   for (int g = threadIdx.x; g <= G; g += kPermThreads) offsets[g] = s_off[g];
   for (int g = threadIdx.x; g < G; g += kPermThreads) {
     const int n = s_off[g + 1] - s_off[g];
-    const int full = n / kTileRows, rem = n % kTileRows;
+    const int nsmall = s_small[g];
+    const int big_rows = n - nsmall;
+    // big tiles of g: rows [s_off[g], s_off[g] + big_rows) in pieces of 256 (last one partial)
+    int32_t* bdst = sched + big_start + (size_t)s_big[g] * kTileInts;
+    for (int i = 0; i * kBigTileRows < big_rows; ++i) {
+      bdst[i * kTileInts + 0] = g;
+      bdst[i * kTileInts + 1] = s_off[g] + i * kBigTileRows;
+      bdst[i * kTileInts + 2] = min(kBigTileRows, big_rows - i * kBigTileRows);
+      bdst[i * kTileInts + 3] = 0;
+    }
+    // small tiles of g: the remaining rows
+    const int row_base = s_off[g] + big_rows;
+    const int full = nsmall / kTileRows, rem = nsmall % kTileRows;
     int32_t* dst = sched + kSchedHeader + (size_t)s_tile[g] * kTileInts;
     for (int i = 0; i < full; ++i) {
       dst[i * kTileInts + 0] = g;
-      dst[i * kTileInts + 1] = s_off[g] + i * kTileRows;
+      dst[i * kTileInts + 1] = row_base + i * kTileRows;
       dst[i * kTileInts + 2] = kTileRows;
       dst[i * kTileInts + 3] = 0;
     }
     if (rem) {
       // rank among partial tiles of the same height: groups below g with that height
       int before = 0;
-      for (int h = 0; h < g; ++h) before += ((s_off[h + 1] - s_off[h]) % kTileRows) == rem;
+      for (int h = 0; h < g; ++h) before += (s_small[h] % kTileRows) == rem;
       int32_t* t = sched + kSchedHeader + (size_t)(s_hist[rem] + before) * kTileInts;
       t[0] = g;
-      t[1] = s_off[g] + full * kTileRows;
+      t[1] = row_base + full * kTileRows;
       t[2] = rem;
       t[3] = 0;
     }
@@ -203,7 +237,7 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const void* __restrict_
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const size_t lds = permute_lds_bytes(a.T, a.E);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, stream, a.topk_ids, a.offsets, a.row_token,
-                     a.token_row, a.sched, a.T, a.E, a.k, a.S);
+                     a.token_row, a.sched, a.T, a.E, a.k, a.S, a.big_on ? 1 : 0, a.big_start);
   return hipGetLastError();
 }
 

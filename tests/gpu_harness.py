@@ -167,9 +167,11 @@ class GpuLayer:
         return buf(self.layer, "token_row", np.int32, (self.T, self.spec.top_k + self.spec.n_shared))
 
     def sched(self):
-        n = buf(self.layer, "sched", np.int32, (1,))[0]
-        s = buf(self.layer, "sched", np.int32, (32 + 4 * n,))
-        return s[:32], s[32:].reshape(n, 4)
+        """(header, small tiles [n][4], big tiles [m][4]) of the tile schedule."""
+        head = buf(self.layer, "sched", np.int32, (32,))
+        n_small, n_big, big_start = int(head[0]), int(head[3]), int(head[4])
+        s = buf(self.layer, "sched", np.int32, (max(32 + 4 * n_small, big_start + 4 * n_big),))
+        return head, s[32:32 + 4 * n_small].reshape(n_small, 4), s[big_start:big_start + 4 * n_big].reshape(n_big, 4)
 
     def h(self):
         dt = h_dtype(self.spec)
