@@ -24,8 +24,9 @@ constexpr int kSchedHeader = 32;
 constexpr int kSchedSmall = 0, kSchedGroups = 1, kSchedRows = 2, kSchedBig = 3, kSchedBigStart = 4;
 constexpr int kTileInts = 4;
 constexpr int kTileRows = 64;       // at most 64 rows of one group per small tile
-constexpr int kBigTileRows = 256;   // rows per big tile
+constexpr int kBigTileRows = 128;   // rows per big tile
 constexpr int kBigTileMin = 128;    // a group needs at least this many rows for big tiles
+constexpr int kBigPartMin = 64;     // a remainder of at least this many rows is one more, partial, big tile
 constexpr int kBigTileMinTokens = 1024;  // big tiles are used for calls with T >= this
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 
@@ -38,6 +39,40 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// 4-bit block decoding.  A code placed in bits 0..3 (or 4..7) of an fp16 half
+// reads as the denormal q * 2^-24 (or q * 2^-20), so one fused multiply-add
+// with the block scale pre-multiplied by 2^24 (or 2^20) gives
+// fp32(scale * q + min) with a single rounding -- the value the block format
+// defines (scale * q is exact in fp32) -- without converting q to float.
+struct Q4Block {
+  float s24, s20, mn;  // scale * 2^24, scale * 2^20, min
+};
+__device__ __forceinline__ Q4Block q4_block(uint32_t scale_bits, uint32_t min_bits) {
+  const float sc = half_bits_to_f32(scale_bits);
+  return Q4Block{sc * 16777216.0f, sc * 1048576.0f, half_bits_to_f32(min_bits)};
+}
+__device__ __forceinline__ float q4_half_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)v); }
+__device__ __forceinline__ float q4_half_hi(uint32_t v) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+// Eight codes of one 32-bit word (code n at bits 4n) -> 8 bf16 values in the
+// MFMA operand order (element j in half j % 2 of register j / 2).
+__device__ __forceinline__ u32x4 q4_decode8(uint32_t w, const Q4Block& b) {
+  const uint32_t w8 = w >> 8;
+  // codes (low half | high half): m0 0|4, m1 1|5 (x16), m2 2|6, m3 3|7 (x16)
+  const uint32_t m0 = w & 0x000f000fu, m1 = w & 0x00f000f0u, m2 = w8 & 0x000f000fu, m3 = w8 & 0x00f000f0u;
+  u32x4 f;
+  f[0] = pack_bf16x2(fmaf(b.s24, q4_half_lo(m0), b.mn), fmaf(b.s20, q4_half_lo(m1), b.mn));
+  f[1] = pack_bf16x2(fmaf(b.s24, q4_half_lo(m2), b.mn), fmaf(b.s20, q4_half_lo(m3), b.mn));
+  f[2] = pack_bf16x2(fmaf(b.s24, q4_half_hi(m0), b.mn), fmaf(b.s20, q4_half_hi(m1), b.mn));
+  f[3] = pack_bf16x2(fmaf(b.s24, q4_half_hi(m2), b.mn), fmaf(b.s20, q4_half_hi(m3), b.mn));
+  return f;
 }
 
 // Plain 16-byte global loads through the vector memory path.

@@ -64,28 +64,10 @@ struct Kp {  // kernel parameters
   int K, N, T, R;
 };
 
-__device__ __forceinline__ float half_bits_to_f32(uint16_t h) {
-  return (float)__builtin_bit_cast(_Float16, h);
-}
-
-// Eight 4-bit codes (one 32-bit word, code n at bits 4n) -> 8 bf16 of scale * q + min
-// (q * scale is exact in fp32, so the fma rounds once, like scale * q + min).
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float sc, float mn) {
-  const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-  u32x4 r;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const float v0 = fmaf(sc, (float)((lo >> (8 * b)) & 0xffu), mn);
-    const float v1 = fmaf(sc, (float)((hi >> (8 * b)) & 0xffu), mn);
-    r[b] = pack_bf16x2(v0, v1);
-  }
-  return r;
-}
-
 // Weight operand of one stage for one 16-row block (A operand).
 struct AStage {
   u32x4 v;               // raw 16 bytes
-  float sc, mn;          // 4-bit block parameters
+  Q4Block blk;           // 4-bit block parameters
 };
 
 template <int WF>
@@ -100,8 +82,7 @@ __device__ __forceinline__ void load_a(AStage& s, const Kp& p, size_t wrow, int 
     // lane group q holds the whole 32-code block k0/32 + q
     s.v = ld16((const uint8_t*)p.w + wrow * (size_t)(p.K / 2) + k0 / 2 + 16 * q);
     const size_t b = wrow * (size_t)(p.K / 32) + k0 / 32 + q;
-    s.sc = half_bits_to_f32(((const uint16_t*)p.w_scale)[b]);
-    s.mn = half_bits_to_f32(((const uint16_t*)p.w_min)[b]);
+    s.blk = q4_block(((const uint16_t*)p.w_scale)[b], ((const uint16_t*)p.w_min)[b]);
   }
 }
 
@@ -137,7 +118,7 @@ __device__ __forceinline__ void mma_stage(Acc<WF> (&acc)[NA][NSUB], const AStage
     if constexpr (WF == kQ4) {
       u32x4 w[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) w[m] = dequant8(a[n].v[m], a[n].sc, a[n].mn);
+      for (int m = 0; m < 4; ++m) w[m] = q4_decode8(a[n].v[m], a[n].blk);
 #pragma unroll
       for (int s = 0; s < NSUB; ++s)
 #pragma unroll

@@ -2,33 +2,46 @@
 // gate/up + SwiGLU and down over the big tiles of the schedule, bf16 or 4-bit
 // block weights.
 //
-// Where a group has hundreds of rows the layer is bound by the matrix cores,
-// not by weight bytes, and the weight operand must be reused over many tokens
-// from on-chip memory.  A block owns 128 weight rows x 256 token rows; both
-// operands of each 64-wide K stage are staged in LDS (double-buffered: the
-// next stage's global loads are in flight while the current one computes);
-// 4-bit codes are dequantised to bf16 once per block by the thread that loads
-// them, before they reach LDS, so each weight is decoded once per 256 tokens.
-// Four waves each compute a 64 x 128 tile with v_mfma_f32_16x16x32_bf16.
+// Where a group has a hundred rows or more the layer is bound by the matrix
+// cores, not by weight bytes.  A block owns 256 weight rows x 128 token rows
+// and walks K in super-stages of 128:
+//  * the token rows (operand B, shared by all four waves) are copied from
+//    global memory straight into LDS with global_load_lds_dwordx4, into a ring
+//    of three stages, in a row-major layout whose 16-byte chunks are
+//    XOR-swizzled by row so that fragment reads avoid bank conflicts;
+//  * each wave owns 64 weight rows (operand A) and loads them from global
+//    memory directly into registers in the MFMA fragment layout, into a ring
+//    of three register tiles; 4-bit codes are dequantised in registers right
+//    before the MFMAs that use them, so every weight byte is read and decoded
+//    once per block and never passes through LDS;
+//  * the loads of super-stage S + 2 are issued before S is computed, so two
+//    super-stages of loads are in flight behind the MFMAs;
+//  * v_mfma_f32_16x16x32_bf16 accumulates a 64 x 128 tile per wave in AGPRs.
+// For 4-bit weights the K order inside a super-stage is permuted so that each
+// lane's 16-byte load is one whole 32-code block (one scale, one min); the
+// token fragments are read from LDS in the same order, which leaves the dot
+// products unchanged.
 //
 // The shared expert and every routed expert go through the same launch; the
 // grouping itself is the point of the pages' "concatenated-expert" fix
 // ("~2.7s fixed per-request TTFT ... concatenated-expert GEMM", section "The
 // fix") and of "the lever is M>1" ("MoE Decode Partition and Submit Floor",
 // M2 update).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kBN = 128;                 // weight rows per block
+constexpr int kBN = 256;                 // weight rows per block (4 waves x 64)
 constexpr int kBM = kBigTileRows;        // token rows per block
-constexpr int kBK = 64;                  // K per stage
-constexpr int kRow = kBK * 2 + 16;       // LDS bytes per staged row (bf16 + 16 B pad)
-constexpr int kStageBytes = (kBN + kBM) * kRow;
+constexpr int kSK = 128;                 // K per super-stage
+constexpr int kBStage = kBM * kSK * 2;   // LDS bytes of one B stage (32 KB)
+constexpr int kRing = 3;                 // super-stages resident (LDS stages and A register tiles)
 constexpr int kThreads = 256;
-constexpr int kDepth = 4;              // stages of global loads in flight
+static_assert(kBM == 128, "the B loader covers 128 rows with 4 waves x 8 DMA instructions x 4 rows");
 
 struct Bp {
   const void* act;          // x [T][K] (gate/up, gathered by row_token) or h [R][K] (down), bf16
@@ -38,37 +51,14 @@ struct Bp {
   const void* w_scale;
   const void* w_min;
   void* out;                // h [R][N] or y [R][N], bf16
-  int K, N, T;
+  int K, N, T, R;
 };
 
-__device__ __forceinline__ float half_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ uint32_t deq2(uint32_t lo_byte, uint32_t hi_byte, float sc, float mn) {
-  return pack_bf16x2(fmaf(sc, (float)lo_byte, mn), fmaf(sc, (float)hi_byte, mn));
-}
-
-// Weight row (index into [G][rows][K]) of staged A row j of a block.
-template <bool kGU>
-__device__ __forceinline__ size_t a_row(const Bp& p, int group, int n0, int j) {
-  if constexpr (kGU) {
-    // 64 gate/up pairs: wave half wn = j / 64 holds gate rows n0+32wn .. +31, then the matching up rows.
-    const int wn = j / 64, jj = j % 64;
-    const int i = n0 + 32 * wn + (jj % 32);
-    return (size_t)group * 2 * p.N + (jj < 32 ? i : p.N + i);
-  } else {
-    return (size_t)group * p.N + n0 + j;
-  }
-}
-
-template <int WF>
-struct AReg {
-  u32x4 v[WF == kQ4 ? 1 : 4];
-  uint32_t sc, mn;  // fp16 bits (zero-extended), converted when the stage is stored
-};
-
-// The prefetch loads are issued as opaque vector loads so the compiler cannot
-// sink them next to their use (which would expose the full memory latency at
-// every stage); completion is awaited explicitly with s_waitcnt vmcnt.
+// A-operand loads are opaque to the compiler so that they stay where they are
+// issued (two super-stages ahead of their use) instead of being sunk next to
+// it; completion is awaited with explicit s_waitcnt vmcnt.
 __device__ __forceinline__ u32x4 gload16(const void* p) {
   u32x4 r;
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
@@ -79,92 +69,195 @@ __device__ __forceinline__ uint32_t gload_u16(const void* p) {
   asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
   return r;
 }
-// Vector-memory loads each thread issues per stage.
-template <int WF>
-constexpr int loads_per_stage() { return WF == kQ4 ? 1 + 2 + 8 : 4 + 8; }
 
-// Wait until this thread's loads of all but the newest n stages have landed.
-template <int WF, int n>
-__device__ __forceinline__ void wait_stages() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(n * loads_per_stage<WF>()) : "memory");
-}
-// Make later uses of a stage's registers depend on the wait above.
+// Vector-memory loads each thread issues per super-stage (8 LDS DMA + A).
 template <int WF>
-__device__ __forceinline__ void tie(AReg<WF>& a, u32x4 (&b)[8]) {
-#pragma unroll
-  for (int i = 0; i < (WF == kQ4 ? 1 : 4); ++i) asm volatile("" : "+v"(a.v[i]));
-  if constexpr (WF == kQ4) asm volatile("" : "+v"(a.sc), "+v"(a.mn));
-#pragma unroll
-  for (int c = 0; c < 8; ++c) asm volatile("" : "+v"(b[c]));
-}
+constexpr int loads_per_stage() { return WF == kQ4 ? 8 + 4 + 8 : 8 + 16; }
 
-// Global -> registers for one stage.  A: thread t covers row t / 2, half t % 2
-// of the stage (32 K); B: thread t covers token row t (64 K).
-template <int WF, bool kGU>
-__device__ __forceinline__ void load_stage(const Bp& p, AReg<WF>& a, u32x4 (&b)[8], size_t arow, size_t brow,
-                                           int k0) {
-  const int half = threadIdx.x % 2;
+// One wave's A operand for one super-stage: 4 fragments of 16 weight rows.
+//   4-bit: lane (r, q) holds the 16 bytes of block q of the super-stage
+//          (codes k = 32q .. 32q+31) and that block's scale and min;
+//   bf16:  lane (r, q) holds, for step kk, elements k = 32kk + 8q .. +7.
+template <int WF>
+struct ATile {
+  u32x4 v[4][WF == kQ4 ? 1 : 4];
+  uint32_t sc[4], mn[4];  // 4-bit only: fp16 bits
+};
+
+// Part g (0..7) of one super-stage's A loads (the loads are spread over the
+// eight MFMA groups of the previous super-stage).  4-bit: group g loads the
+// scale (g even) or min (g odd) of fragment g / 2, and the codes of fragment
+// g / 2 on even g; bf16: fragment g / 2, steps 2 (g % 2) and 2 (g % 2) + 1.
+template <int WF>
+__device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const size_t (&arow)[4], int S, int q, int g) {
+  const int b = g / 2;
   if constexpr (WF == kQ4) {
-    const int kb = k0 + 32 * half;  // one 32-code block
-    a.v[0] = gload16((const uint8_t*)p.w + arow * (size_t)(p.K / 2) + kb / 2);
-    const size_t blk = arow * (size_t)(p.K / 32) + kb / 32;
-    a.sc = gload_u16((const uint16_t*)p.w_scale + blk);
-    a.mn = gload_u16((const uint16_t*)p.w_min + blk);
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) a.v[c] = gload16((const uint16_t*)p.w + arow * p.K + k0 + 32 * half + 8 * c);
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) b[c] = gload16((const uint16_t*)p.act + brow * p.K + k0 + 8 * c);
-}
-
-// Registers -> LDS for one stage (4-bit codes decoded here, once per block).
-template <int WF>
-__device__ __forceinline__ void store_stage(uint8_t* st, const AReg<WF>& a, const u32x4 (&b)[8]) {
-  const int t = threadIdx.x;
-  uint8_t* arow = st + (t / 2) * kRow + 64 * (t % 2);
-  if constexpr (WF == kQ4) {
-    const float sc = half_bits_to_f32((uint16_t)a.sc), mn = half_bits_to_f32((uint16_t)a.mn);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t w = a.v[0][m];  // codes 8m .. 8m+7 of the block
-      const uint32_t lo = w & 0x0f0f0f0fu, hi = (w >> 4) & 0x0f0f0f0fu;
-      u32x4 d;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) d[q] = deq2((lo >> (8 * q)) & 0xffu, (hi >> (8 * q)) & 0xffu, sc, mn);
-      *reinterpret_cast<u32x4*>(arow + 16 * m) = d;
+    const size_t blk = arow[b] * (size_t)(p.K / 32) + S * (kSK / 32) + q;
+    if (g % 2 == 0) {
+      a.v[b][0] = gload16((const uint8_t*)p.w + arow[b] * (size_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
+      a.sc[b] = gload_u16((const uint16_t*)p.w_scale + blk);
+    } else {
+      a.mn[b] = gload_u16((const uint16_t*)p.w_min + blk);
     }
   } else {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) *reinterpret_cast<u32x4*>(arow + 16 * c) = a.v[c];
+    for (int kk = 2 * (g % 2); kk < 2 * (g % 2) + 2; ++kk)
+      a.v[b][kk] = gload16((const uint16_t*)p.w + arow[b] * p.K + S * kSK + 32 * kk + 8 * q);
   }
-  uint8_t* brow = st + (kBN + t) * kRow;
+}
+
+// Make every later use of a tile's registers depend on the preceding wait.
+template <int WF>
+__device__ __forceinline__ void tie(ATile<WF>& a) {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(brow + 16 * c) = b[c];
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int i = 0; i < (WF == kQ4 ? 1 : 4); ++i) asm volatile("" : "+v"(a.v[b][i]));
+    if constexpr (WF == kQ4) asm volatile("" : "+v"(a.sc[b]), "+v"(a.mn[b]));
+  }
+}
+
+// B operand of one super-stage -> LDS, DMA instruction i of the wave: it
+// writes the 1 KB at (8 wave + i) KB of the stage: rows 32 wave + 4i + lane / 16,
+// chunk slot lane % 16, which holds the row's chunk slot ^ (row % 16).
+__device__ __forceinline__ void load_b_part(uint8_t* stage, const uint8_t* const (&src)[8], int S, int wave, int i) {
+  __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)S * (kSK * 2)),
+                                   (lds_void*)(stage + (8 * wave + i) * 1024), 16, 0, 0);
+}
+
+// Barrier between super-stages.  __syncthreads() would also fence the
+// pending LDS DMA (the loads two super-stages ahead) and so drain the ring;
+// here each wave waits only for its own LDS reads (the slot they read is
+// refilled after the barrier), and the DMA data of the next super-stage is
+// covered by the explicit vmcnt wait before the barrier.  The memory clobbers
+// keep the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Chunk (16 bytes = 8 K) of a token row that lane group q reads for step kk.
+template <int WF>
+__device__ __forceinline__ int b_chunk(int q, int kk) { return WF == kQ4 ? 4 * q + kk : 4 * kk + q; }
+
+// A fragment of step kk for weight block b.  4-bit: the dword holds codes
+// 8kk .. 8kk+7 of the lane's block, two per byte (even code in the low nibble).
+template <int WF>
+__device__ __forceinline__ u32x4 a_frag(const ATile<WF>& a, const Q4Block (&qs)[4], int b, int kk) {
+  if constexpr (WF == kQ4) {
+    return q4_decode8(a.v[b][0][kk], qs[b]);  // codes 8kk .. 8kk+7 of the lane's block
+  } else {
+    return a.v[b][kk];
+  }
+}
+
+// One super-stage of MFMAs, software-pipelined in 8 groups (step kk = g / 2,
+// token blocks 4 (g % 2) .. +3): the B fragments of group g + 1 are read from
+// LDS before the 16 MFMAs of group g are issued, and the A fragments of the
+// next step are decoded alongside them, so neither the LDS latency nor the
+// decode stalls the matrix pipe.  Part g of the global loads of a later
+// super-stage (issue_part(g)) is issued with group g, so that the memory
+// pipeline fills while the MFMAs run instead of in one burst.  sched_barrier
+// pins that order.
+template <int WF, class IssuePart>
+__device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[4][8], int lr, int q,
+                                        IssuePart&& issue_part) {
+  Q4Block qs[4];
+  if constexpr (WF == kQ4) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) qs[b] = q4_block(a.sc[b], a.mn[b]);
+  }
+  // token row 16c + lr, chunk slot b_chunk ^ lr (the row's low 4 bits are lr)
+  auto bfrag = [&](int kk, int c) {
+    return *reinterpret_cast<const u32x4*>(st + (16 * c + lr) * (kSK * 2) + 16 * (b_chunk<WF>(q, kk) ^ lr));
+  };
+  u32x4 af[4], bf[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) bf[i] = bfrag(0, i);
+#pragma unroll
+  for (int g = 0; g < 8; ++g) {
+    const int kk = g / 2, c0 = 4 * (g % 2);
+    const bool next_a = g % 2 == 1 && kk < 3;
+    u32x4 nb[4], na[4];
+    if (g < 7) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nb[i] = bfrag((g + 1) / 2, 4 * ((g + 1) % 2) + i);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    issue_part(g);
+    if (next_a) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) na[b] = a_frag<WF>(a, qs, b, kk + 1);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) acc[b][c0 + i] = mfma_bf16_16x16x32(af[b], bf[i], acc[b][c0 + i]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (g < 7) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bf[i] = nb[i];
+    }
+    if (next_a) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) af[b] = na[b];
+    }
+  }
 }
 
 __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
 
+// 4-bit: two blocks per CU (two waves per SIMD hide each other's LDS and
+// dequant latency); bf16 keeps both A super-stages in registers, one block.
+template <int WF>
+constexpr int big_waves_per_simd() { return 1; }
+
 template <int WF, bool kGU>
-__global__ __launch_bounds__(kThreads) void big_gemm_kernel(Bp p) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStageBytes];
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(big_waves_per_simd<WF>())))
+void big_gemm_kernel(Bp p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBStage];
   const int n_big = p.sched[kSchedBig];
   const int cols = kGU ? kBN / 2 : kBN;  // output columns per block
   const int per_tile = p.N / cols;
-  const int w = blockIdx.x;
-  if (w >= n_big * per_tile) return;
-  const int mt = w / per_tile, nt = w % per_tile;
+  const int items = n_big * per_tile;
+  // Items are dealt to XCDs in contiguous runs (block b runs on XCD b % 8), so
+  // the column blocks of one row tile -- which read the same token rows -- and
+  // the row tiles of one expert share an L2.
+  const int per_xcd = (items + kXcds - 1) / kXcds;
+  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (blockIdx.x / kXcds >= per_xcd || item >= items) return;
+  const int mt = item / per_tile, nt = item % per_tile;
   const int32_t* tile = p.sched + p.sched[kSchedBigStart] + (size_t)mt * kTileInts;
   const int group = tile[0], row0 = tile[1], rows = tile[2];
   const int n0 = nt * cols;
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int lr = lane % 16, q = lane / 16;
-  const int wn = wave & 1, wm = wave >> 1;
-  // loader rows
-  const size_t arow = a_row<kGU>(p, group, n0, t / 2);
-  const int rr = t < rows ? row0 + t : row0;
-  const size_t brow = kGU ? (size_t)min(max(p.row_token[rr], 0), p.T - 1) : (size_t)rr;
+
+  // A rows of this wave's 4 fragments (GU: gate cols i0.., i0+16.., then the up rows).
+  size_t arow[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if constexpr (kGU) {
+      const int i = n0 + 32 * wave + 16 * (b & 1) + lr;
+      arow[b] = (size_t)group * 2 * p.N + (b < 2 ? i : p.N + i);
+    } else {
+      arow[b] = (size_t)group * p.N + n0 + 64 * wave + 16 * b + lr;
+    }
+  }
+  // B sources of this lane's 8 DMA chunks (rows past the tile repeat row 0).
+  const uint8_t* bsrc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int rr = 32 * wave + 4 * i + lane / 16;
+    const int r = rr < rows ? row0 + rr : row0;
+    const size_t src_row = kGU ? (size_t)min(max(p.row_token[r], 0), p.T - 1) : (size_t)r;
+    const int chunk = (lane % 16) ^ (rr % 16);
+    bsrc[i] = (const uint8_t*)p.act + src_row * (size_t)p.K * 2 + 16 * chunk;
+  }
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -172,61 +265,64 @@ __global__ __launch_bounds__(kThreads) void big_gemm_kernel(Bp p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Register ring of kDepth stages: the global loads of stage s + kDepth are
-  // issued while stage s computes, so kDepth stages of loads are in flight.
-  AReg<WF> areg[kDepth];
-  u32x4 breg[kDepth][8];
-  // K is a multiple of 256, so the stage count is a multiple of the ring depth.
-  // Every iteration refills one slot (near the end with the last stage again,
-  // an L2 hit), which keeps the number of loads in flight the same everywhere
-  // and lets each wait be a constant.
-  const int nk = p.K / kBK;
+  // Ring of kRing super-stages.  step(S, j) computes S from slot j while
+  // issuing the loads of S + 2 (clamped to the last super-stage, so that every
+  // step issues the same number of loads and the wait below is a constant)
+  // into slot (j + 2) % 3, which S - 1 used and the barrier closing S - 1 freed.
+  ATile<WF> at[kRing];
+  const int nS = p.K / kSK;
+  constexpr int L = loads_per_stage<WF>();
+  auto issue = [&](int S, int j) {
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load_stage<WF, kGU>(p, areg[d], breg[d], arow, brow, d * kBK);
-  wait_stages<WF, kDepth - 1>();
-  tie<WF>(areg[0], breg[0]);
-  store_stage<WF>(lds, areg[0], breg[0]);
-  __syncthreads();
-  for (int s0 = 0; s0 < nk; s0 += kDepth) {
-#pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      const int s = s0 + d;
-      // slot d held stage s, already in LDS: refill it
-      load_stage<WF, kGU>(p, areg[d], breg[d], arow, brow, min(s + kDepth, nk - 1) * kBK);
-      const uint8_t* st = lds + (s & 1) * kStageBytes;
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        u32x4 af[4];
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-          af[b] = *reinterpret_cast<const u32x4*>(st + (wn * 64 + 16 * b + lr) * kRow + kk * 64 + 16 * q);
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const u32x4 bf =
-              *reinterpret_cast<const u32x4*>(st + (kBN + wm * 128 + 16 * c + lr) * kRow + kk * 64 + 16 * q);
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[b][c] = mfma_bf16_16x16x32(af[b], bf, acc[b][c]);
-        }
-      }
-      // stage s + 1 sits in slot dn; the kDepth - 1 stages issued after it stay in flight
-      const int dn = (d + 1) % kDepth;
-      wait_stages<WF, kDepth - 1>();
-      tie<WF>(areg[dn], breg[dn]);
-      if (s + 1 < nk) store_stage<WF>(lds + ((s + 1) & 1) * kStageBytes, areg[dn], breg[dn]);
-      __syncthreads();
+    for (int g = 0; g < 8; ++g) {
+      load_b_part(lds + j * kBStage, bsrc, S, wave, g);
+      load_a_part<WF>(p, at[j], arow, S, q, g);
     }
+  };
+  issue(0, 0);
+  issue(min(1, nS - 1), 1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");  // super-stage 0 landed
+  tie<WF>(at[0]);
+  stage_barrier();
+  auto step = [&](int S, auto slot) {
+    constexpr int j = decltype(slot)::value;
+    const int S2 = min(S + 2, nS - 1);
+    compute<WF>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) {
+      load_b_part(lds + ((j + 2) % kRing) * kBStage, bsrc, S2, wave, g);
+      load_a_part<WF>(p, at[(j + 2) % kRing], arow, S2, q, g);
+    });
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");  // super-stage S + 1 landed
+    tie<WF>(at[(j + 1) % kRing]);
+    stage_barrier();
+  };
+  // Whole rounds of the ring, then the remaining one or two super-stages
+  // (nested, so that every path through the waits is one the ring takes).
+  int S = 0;
+  for (; S + kRing <= nS; S += kRing) {
+    step(S, std::integral_constant<int, 0>{});
+    step(S + 1, std::integral_constant<int, 1>{});
+    step(S + 2, std::integral_constant<int, 2>{});
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the ring's last refills, before its registers are reused
-  // Epilogue: block b's D[i][j] is in lane j + 16 * (i / 4), register i % 4.
+  if (S < nS) {
+    step(S, std::integral_constant<int, 0>{});
+    if (S + 1 < nS) step(S + 1, std::integral_constant<int, 1>{});
+  }
+  // Drain the last (clamped) refills.  Their registers are tied after the wait
+  // so that the compiler keeps them reserved until the loads have landed.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < kRing; ++j) tie<WF>(at[j]);
+  // Epilogue: fragment b's D[i][j] (i: weight row, j: token) is in lane
+  // j + 16 * (i / 4), register i % 4.
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
-    const int tr = wm * 128 + 16 * c + lr;
+    const int tr = 16 * c + lr;
     if (tr >= rows) continue;
     const int r = row0 + tr;
     if constexpr (kGU) {
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
-        const int col = n0 + 32 * wn + 16 * b + 4 * q;
+        const int col = n0 + 32 * wave + 16 * b + 4 * q;
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = silu_fast(acc[b][c][i]) * acc[b + 2][c][i];
@@ -236,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void big_gemm_kernel(Bp p) {
     } else {
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        const int col = n0 + 64 * wn + 16 * b + 4 * q;
+        const int col = n0 + 64 * wave + 16 * b + 4 * q;
         u32x2 o = {pack_bf16x2(acc[b][c][0], acc[b][c][1]), pack_bf16x2(acc[b][c][2], acc[b][c][3])};
         *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
       }
@@ -247,9 +343,12 @@ __global__ __launch_bounds__(kThreads) void big_gemm_kernel(Bp p) {
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   if (a.wfmt != kBF16 && a.wfmt != kQ4) return hipErrorInvalidValue;
-  Bp p{a.act, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T};
   const int cols = kGU ? kBN / 2 : kBN;
-  const int64_t items = ((int64_t)a.R / kBigTileMin + 1) * (a.N / cols);  // each big tile has >= 128 rows
+  if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
+  Bp p{a.act, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
+  // every big tile holds at least kBigPartMin rows; a multiple of 8 so every XCD gets the same slots
+  int64_t items = ((int64_t)a.R / kBigPartMin + 1) * (a.N / cols);
+  items = (items + kXcds - 1) / kXcds * kXcds;
   if (items > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   if (a.wfmt == kQ4)
     hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU>), dim3(items), dim3(kThreads), 0, stream, p);

@@ -27,7 +27,7 @@ struct PermuteArgs {
   int32_t* token_row;
   int32_t* sched;
   int T, E, k, S;
-  bool big_on;    // cut groups of >= 128 rows into 256-row big tiles
+  bool big_on;    // cut groups of >= 128 rows into 128-row big tiles
   int big_start;  // int index of the big-tile list in the schedule
 };
 
@@ -87,9 +87,9 @@ inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)((T + 31)
 constexpr size_t kPermuteMaxLds = 60 * 1024;
 
 // Tile schedule capacity for R_max rows over G groups: small tiles first,
-// then the big-tile list (at most one big tile per 128 rows).
+// then the big-tile list (every big tile holds at least 64 rows).
 inline size_t sched_small_cap(int64_t r_max, int64_t G) { return (size_t)((r_max + 63) / 64 + G); }
 inline size_t sched_big_start(int64_t r_max, int64_t G) { return 32 + 4 * sched_small_cap(r_max, G); }
-inline size_t sched_ints(int64_t r_max, int64_t G) { return sched_big_start(r_max, G) + 4 * (size_t)(r_max / 128 + 1); }
+inline size_t sched_ints(int64_t r_max, int64_t G) { return sched_big_start(r_max, G) + 4 * (size_t)(r_max / 64 + 1); }
 
 }  // namespace moe

@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
   __syncthreads();
   // 3. offsets over groups, then the two tile lists (wave 0 scans; each lane
   //    takes 5 consecutive groups).  With big tiles on, a group of >= 128 rows
-  //    is cut into tiles of 256 rows (a remainder of >= 128 rows is one more,
+  //    is cut into tiles of 128 rows (a remainder of >= 64 rows is one more,
   //    partial, big tile; a smaller remainder goes to small tiles).  Small
   //    tiles hold <= 64 rows: all full ones first (by group), then the partial
   //    ones by descending height (ties by group) -- heavy tiles first.
@@ -101,8 +101,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
       const int n = g < G ? s_cnt[g] : 0;
       int nbig = 0, nsmall = n;
       if (big_on && n >= kBigTileMin) {
-        nbig = n / kBigTileRows + (n % kBigTileRows >= kBigTileMin ? 1 : 0);
-        nsmall = n % kBigTileRows >= kBigTileMin ? 0 : n % kBigTileRows;
+        nbig = n / kBigTileRows + (n % kBigTileRows >= kBigPartMin ? 1 : 0);
+        nsmall = n % kBigTileRows >= kBigPartMin ? 0 : n % kBigTileRows;
       }
       rows_sum += n;
       full_sum += nsmall / kTileRows;
@@ -119,8 +119,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
         const int n = s_cnt[g];
         int nbig = 0, nsmall = n;
         if (big_on && n >= kBigTileMin) {
-          nbig = n / kBigTileRows + (n % kBigTileRows >= kBigTileMin ? 1 : 0);
-          nsmall = n % kBigTileRows >= kBigTileMin ? 0 : n % kBigTileRows;
+          nbig = n / kBigTileRows + (n % kBigTileRows >= kBigPartMin ? 1 : 0);
+          nsmall = n % kBigTileRows >= kBigPartMin ? 0 : n % kBigTileRows;
         }
         s_off[g] = r;
         s_tile[g] = f;  // first full small tile of g
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
     const int n = s_off[g + 1] - s_off[g];
     const int nsmall = s_small[g];
     const int big_rows = n - nsmall;
-    // big tiles of g: rows [s_off[g], s_off[g] + big_rows) in pieces of 256 (last one partial)
+    // big tiles of g: rows [s_off[g], s_off[g] + big_rows) in pieces of 128 (last one partial)
     int32_t* bdst = sched + big_start + (size_t)s_big[g] * kTileInts;
     for (int i = 0; i * kBigTileRows < big_rows; ++i) {
       bdst[i * kTileInts + 0] = g;

@@ -42,8 +42,8 @@ SMALL = [
     ("i8_e32k8s1_t71", 512, 256, 32, 8, 1, 71, "i8", 0.0),
     ("q4_e16k4s1_t100_zipf", 256, 256, 16, 4, 1, 100, "q4", 1.1),
     ("q4_e16k2s1_t9", 512, 256, 16, 2, 1, 9, "q4", 0.0),
-    # T >= 1024: groups of >= 128 rows go through the big-tile kernels (full 256-row
-    # tiles, a partial big tile when >= 128 rows remain, small tiles for the rest)
+    # T >= 1024: groups of >= 128 rows go through the big-tile kernels (full 128-row
+    # tiles, a partial big tile when >= 64 rows remain, small tiles for the rest)
     ("bf16_e8k2s1_t1200_big", 256, 256, 8, 2, 1, 1200, "bf16", 0.0),
     ("q4_e8k2s1_t1100_big", 256, 256, 8, 2, 1, 1100, "q4", 0.0),
     ("q4_e16k4s1_t1024_zipf_big", 256, 512, 16, 4, 1, 1024, "q4", 1.1),
@@ -65,9 +65,9 @@ def check_permute(g, ref_perm):
     np.testing.assert_array_equal(g.token_row(), token_row)
     head, small, big = g.sched()
     # The tiles cover every group's rows exactly once: small tiles of <= 64 rows,
-    # big tiles of 128..256 rows (only when T >= 1024), big tiles first within a group.
+    # big tiles of 64..128 rows (only when T >= 1024), big tiles first within a group.
     covered = np.zeros(offsets[-1], np.int32)
-    for tiles, lo, hi in ((small, 1, 64), (big, 128, 256)):
+    for tiles, lo, hi in ((small, 1, 64), (big, 64, 128)):
         for grp, r0, n, _ in tiles:
             assert lo <= n <= hi and offsets[grp] <= r0 and r0 + n <= offsets[grp + 1]
             covered[r0:r0 + n] += 1
