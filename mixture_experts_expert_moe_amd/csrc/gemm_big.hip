@@ -36,12 +36,15 @@ namespace moe {
 namespace {
 
 constexpr int kBN = 256;                 // weight rows per block (4 waves x 64)
-constexpr int kBM = kBigTileRows;        // token rows per block
 constexpr int kSK = 128;                 // K per super-stage
-constexpr int kBStage = kBM * kSK * 2;   // LDS bytes of one B stage (32 KB)
 constexpr int kRing = 3;                 // super-stages resident (LDS stages and A register tiles)
 constexpr int kThreads = 256;
-static_assert(kBM == 128, "the B loader covers 128 rows with 4 waves x 8 DMA instructions x 4 rows");
+// Token rows per block: kBigTileRows for the big-tile list, kTileRows for the
+// small-tile list.  B stage bytes, and DMA instructions per wave per stage
+// (each covers 4 rows of 256 bytes).
+template <int BM> constexpr int b_stage_bytes() { return BM * kSK * 2; }
+template <int BM> constexpr int b_dma_per_wave() { return BM / 16; }
+static_assert(kBigTileRows == 128 && kTileRows == 64, "tile heights the B loader and fragments are laid out for");
 
 struct Bp {
   const void* act;          // x [T][K] (gate/up, gathered by row_token) or h [R][K] (down), bf16
@@ -70,9 +73,9 @@ __device__ __forceinline__ uint32_t gload_u16(const void* p) {
   return r;
 }
 
-// Vector-memory loads each thread issues per super-stage (8 LDS DMA + A).
-template <int WF>
-constexpr int loads_per_stage() { return WF == kQ4 ? 8 + 4 + 8 : 8 + 16; }
+// Vector-memory loads each thread issues per super-stage (LDS DMA + A).
+template <int WF, int BM>
+constexpr int loads_per_stage() { return b_dma_per_wave<BM>() + (WF == kQ4 ? 4 + 8 : 16); }
 
 // One wave's A operand for one super-stage: 4 fragments of 16 weight rows.
 //   4-bit: lane (r, q) holds the 16 bytes of block q of the super-stage
@@ -117,12 +120,16 @@ __device__ __forceinline__ void tie(ATile<WF>& a) {
   }
 }
 
-// B operand of one super-stage -> LDS, DMA instruction i of the wave: it
-// writes the 1 KB at (8 wave + i) KB of the stage: rows 32 wave + 4i + lane / 16,
-// chunk slot lane % 16, which holds the row's chunk slot ^ (row % 16).
-__device__ __forceinline__ void load_b_part(uint8_t* stage, const uint8_t* const (&src)[8], int S, int wave, int i) {
+// B operand of one super-stage -> LDS, DMA instruction i of the wave (n = BM / 16
+// per wave): it writes the 1 KB at (n wave + i) KB of the stage: rows
+// 4 (n wave + i) + lane / 16, chunk slot lane % 16, which holds the row's
+// chunk slot ^ (row % 16).
+template <int BM>
+__device__ __forceinline__ void load_b_part(uint8_t* stage, const uint8_t* const (&src)[b_dma_per_wave<BM>()], int S,
+                                            int wave, int i) {
+  constexpr int n = b_dma_per_wave<BM>();
   __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)S * (kSK * 2)),
-                                   (lds_void*)(stage + (8 * wave + i) * 1024), 16, 0, 0);
+                                   (lds_void*)(stage + (n * wave + i) * 1024), 16, 0, 0);
 }
 
 // Barrier between super-stages.  __syncthreads() would also fence the
@@ -152,17 +159,18 @@ __device__ __forceinline__ u32x4 a_frag(const ATile<WF>& a, const Q4Block (&qs)[
   }
 }
 
-// One super-stage of MFMAs, software-pipelined in 8 groups (step kk = g / 2,
-// token blocks 4 (g % 2) .. +3): the B fragments of group g + 1 are read from
-// LDS before the 16 MFMAs of group g are issued, and the A fragments of the
-// next step are decoded alongside them, so neither the LDS latency nor the
-// decode stalls the matrix pipe.  Part g of the global loads of a later
-// super-stage (issue_part(g)) is issued with group g, so that the memory
-// pipeline fills while the MFMAs run instead of in one burst.  sched_barrier
-// pins that order.
-template <int WF, class IssuePart>
-__device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[4][8], int lr, int q,
-                                        IssuePart&& issue_part) {
+// One super-stage of MFMAs, software-pipelined in groups of 4 token blocks
+// (NG = BM / 64 groups per step kk): the B fragments of the next group are
+// read from LDS before the 16 MFMAs of the current group are issued, and the
+// A fragments of the next step are decoded alongside them, so neither the LDS
+// latency nor the decode stalls the matrix pipe.  The 8 parts of the global
+// loads of a later super-stage (issue_part(p)) are spread evenly over the
+// groups, so that the memory pipeline fills while the MFMAs run instead of in
+// one burst.  sched_barrier pins that order.
+template <int WF, int BM, class IssuePart>
+__device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[4][BM / 16], int lr,
+                                        int q, IssuePart&& issue_part) {
+  constexpr int NG = BM / 64, G = 4 * NG, PPG = 8 / G;  // groups per step, groups, load parts per group
   Q4Block qs[4];
   if constexpr (WF == kQ4) {
 #pragma unroll
@@ -178,16 +186,17 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
 #pragma unroll
   for (int i = 0; i < 4; ++i) bf[i] = bfrag(0, i);
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
-    const int kk = g / 2, c0 = 4 * (g % 2);
-    const bool next_a = g % 2 == 1 && kk < 3;
+  for (int g = 0; g < G; ++g) {
+    const int kk = g / NG, c0 = 4 * (g % NG);
+    const bool next_a = g % NG == NG - 1 && kk < 3;
     u32x4 nb[4], na[4];
-    if (g < 7) {
+    if (g < G - 1) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) nb[i] = bfrag((g + 1) / 2, 4 * ((g + 1) % 2) + i);
+      for (int i = 0; i < 4; ++i) nb[i] = bfrag((g + 1) / NG, 4 * ((g + 1) % NG) + i);
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue_part(g);
+#pragma unroll
+    for (int pp = 0; pp < PPG; ++pp) issue_part(g * PPG + pp);
     if (next_a) {
 #pragma unroll
       for (int b = 0; b < 4; ++b) na[b] = a_frag<WF>(a, qs, b, kk + 1);
@@ -197,7 +206,7 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
 #pragma unroll
       for (int b = 0; b < 4; ++b) acc[b][c0 + i] = mfma_bf16_16x16x32(af[b], bf[i], acc[b][c0 + i]);
     __builtin_amdgcn_sched_barrier(0);
-    if (g < 7) {
+    if (g < G - 1) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) bf[i] = nb[i];
     }
@@ -210,30 +219,11 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
 
 __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
 
-// 4-bit: two blocks per CU (two waves per SIMD hide each other's LDS and
-// dequant latency); bf16 keeps both A super-stages in registers, one block.
-template <int WF>
-constexpr int big_waves_per_simd() { return 1; }
-
-template <int WF, bool kGU>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(big_waves_per_simd<WF>())))
-void big_gemm_kernel(Bp p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * kBStage];
-  const int n_big = p.sched[kSchedBig];
-  const int cols = kGU ? kBN / 2 : kBN;  // output columns per block
-  const int per_tile = p.N / cols;
-  const int items = n_big * per_tile;
-  // Items are dealt to XCDs in contiguous runs (block b runs on XCD b % 8), so
-  // the column blocks of one row tile -- which read the same token rows -- and
-  // the row tiles of one expert share an L2.
-  const int per_xcd = (items + kXcds - 1) / kXcds;
-  const int item = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
-  if (blockIdx.x / kXcds >= per_xcd || item >= items) return;
-  const int mt = item / per_tile, nt = item % per_tile;
-  const int32_t* tile = p.sched + p.sched[kSchedBigStart] + (size_t)mt * kTileInts;
-  const int group = tile[0], row0 = tile[1], rows = tile[2];
-  const int n0 = nt * cols;
-
+// One item: weight columns [n0, n0 + 256) (gate/up: 128 gate/up pairs) of
+// group `group` against token rows [row0, row0 + rows) (rows <= BM).
+template <int WF, bool kGU, int BM>
+__device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, int row0, int rows, int n0) {
+  constexpr int kBStage = b_stage_bytes<BM>(), NC = BM / 16, NB = b_dma_per_wave<BM>();
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int lr = lane % 16, q = lane / 16;
 
@@ -248,22 +238,22 @@ void big_gemm_kernel(Bp p) {
       arow[b] = (size_t)group * p.N + n0 + 64 * wave + 16 * b + lr;
     }
   }
-  // B sources of this lane's 8 DMA chunks (rows past the tile repeat row 0).
-  const uint8_t* bsrc[8];
+  // B sources of this lane's DMA chunks (rows past the tile repeat row 0).
+  const uint8_t* bsrc[NB];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int rr = 32 * wave + 4 * i + lane / 16;
+  for (int i = 0; i < NB; ++i) {
+    const int rr = 4 * (NB * wave + i) + lane / 16;
     const int r = rr < rows ? row0 + rr : row0;
     const size_t src_row = kGU ? (size_t)min(max(p.row_token[r], 0), p.T - 1) : (size_t)r;
     const int chunk = (lane % 16) ^ (rr % 16);
     bsrc[i] = (const uint8_t*)p.act + src_row * (size_t)p.K * 2 + 16 * chunk;
   }
 
-  f32x4 acc[4][8];
+  f32x4 acc[4][NC];
 #pragma unroll
   for (int b = 0; b < 4; ++b)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < NC; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Ring of kRing super-stages.  step(S, j) computes S from slot j while
   // issuing the loads of S + 2 (clamped to the last super-stage, so that every
@@ -271,13 +261,15 @@ void big_gemm_kernel(Bp p) {
   // into slot (j + 2) % 3, which S - 1 used and the barrier closing S - 1 freed.
   ATile<WF> at[kRing];
   const int nS = p.K / kSK;
-  constexpr int L = loads_per_stage<WF>();
+  constexpr int L = loads_per_stage<WF, BM>();
+  // Part g (0..7) of the loads of super-stage S into slot j.
+  auto part = [&](int S, int j, int g) {
+    if (g < NB) load_b_part<BM>(lds + j * kBStage, bsrc, S, wave, g);
+    load_a_part<WF>(p, at[j], arow, S, q, g);
+  };
   auto issue = [&](int S, int j) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      load_b_part(lds + j * kBStage, bsrc, S, wave, g);
-      load_a_part<WF>(p, at[j], arow, S, q, g);
-    }
+    for (int g = 0; g < 8; ++g) part(S, j, g);
   };
   issue(0, 0);
   issue(min(1, nS - 1), 1);
@@ -287,10 +279,7 @@ void big_gemm_kernel(Bp p) {
   auto step = [&](int S, auto slot) {
     constexpr int j = decltype(slot)::value;
     const int S2 = min(S + 2, nS - 1);
-    compute<WF>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) {
-      load_b_part(lds + ((j + 2) % kRing) * kBStage, bsrc, S2, wave, g);
-      load_a_part<WF>(p, at[(j + 2) % kRing], arow, S2, q, g);
-    });
+    compute<WF, BM>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) { part(S2, (j + 2) % kRing, g); });
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");  // super-stage S + 1 landed
     tie<WF>(at[(j + 1) % kRing]);
     stage_barrier();
@@ -315,7 +304,7 @@ void big_gemm_kernel(Bp p) {
   // Epilogue: fragment b's D[i][j] (i: weight row, j: token) is in lane
   // j + 16 * (i / 4), register i % 4.
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int tr = 16 * c + lr;
     if (tr >= rows) continue;
     const int r = row0 + tr;
@@ -340,26 +329,68 @@ void big_gemm_kernel(Bp p) {
   }
 }
 
+// One block per item.  Items of the big-tile list (128-row tiles) and, for
+// 4-bit weights, of the small-tile list (<= 64 rows) share the launch: block b
+// runs on XCD b % 8, and each XCD takes a contiguous run of the big items
+// first and then a contiguous run of the small items, so the small items fill
+// the CUs that the last big items leave idle, and the column blocks of one
+// row tile (which read the same token rows) share an L2.
+template <int WF, bool kGU, bool kSmall>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+void big_gemm_kernel(Bp p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * b_stage_bytes<kBigTileRows>()];
+  const int cols = kGU ? kBN / 2 : kBN;  // output columns per item
+  const int per_tile = p.N / cols;
+  const int big_items = p.sched[kSchedBig] * per_tile;
+  const int small_items = kSmall ? p.sched[kSchedSmall] * per_tile : 0;
+  const int big_px = (big_items + kXcds - 1) / kXcds, small_px = (small_items + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  if (slot < big_px) {
+    const int item = xcd * big_px + slot;
+    if (item >= big_items) return;
+    const int32_t* tile = p.sched + p.sched[kSchedBigStart] + (size_t)(item / per_tile) * kTileInts;
+    gemm_item<WF, kGU, kBigTileRows>(p, lds, tile[0], tile[1], tile[2], (item % per_tile) * cols);
+  } else if (kSmall && slot < big_px + small_px) {
+    const int item = xcd * small_px + (slot - big_px);
+    if (item >= small_items) return;
+    const int32_t* tile = p.sched + kSchedHeader + (size_t)(item / per_tile) * kTileInts;
+    gemm_item<WF, kGU, kTileRows>(p, lds, tile[0], tile[1], tile[2], (item % per_tile) * cols);
+  }
+}
+
+// One wave per SIMD: the accumulators (64 x 128 per wave) and the A register
+// ring need more than half the register file.  (A spill would also add
+// scratch loads to the vmcnt accounting of the ring.)
 template <bool kGU>
-hipError_t launch(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (a.wfmt != kBF16 && a.wfmt != kQ4) return hipErrorInvalidValue;
+  if (with_small && a.wfmt != kQ4) return hipErrorInvalidValue;  // bf16 small tiles keep the K-split kernel
   const int cols = kGU ? kBN / 2 : kBN;
   if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
   Bp p{a.act, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
-  // every big tile holds at least kBigPartMin rows; a multiple of 8 so every XCD gets the same slots
-  int64_t items = ((int64_t)a.R / kBigPartMin + 1) * (a.N / cols);
-  items = (items + kXcds - 1) / kXcds * kXcds;
-  if (items > (int64_t)INT32_MAX) return hipErrorInvalidValue;
-  if (a.wfmt == kQ4)
-    hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU>), dim3(items), dim3(kThreads), 0, stream, p);
+  // grid: per XCD, slots for an upper bound of each list's items (big tiles
+  // hold >= kBigPartMin rows)
+  const int64_t per_tile = a.N / cols;
+  const int64_t big_px = (((int64_t)a.R / kBigPartMin + 1) * per_tile + kXcds - 1) / kXcds;
+  const int64_t small_px = with_small ? ((int64_t)sched_small_cap(a.R, a.G) * per_tile + kXcds - 1) / kXcds : 0;
+  const int64_t blocks = (big_px + small_px) * kXcds;
+  if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  if (with_small)
+    hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  else if (a.wfmt == kQ4)
+    hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU>), dim3(items), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t stream) { return launch<true>(a, stream); }
-hipError_t launch_big_down(const GemmArgs& a, hipStream_t stream) { return launch<false>(a, stream); }
+hipError_t launch_big_gate_up(const GemmArgs& a, bool with_small, hipStream_t stream) {
+  return launch<true>(a, with_small, stream);
+}
+hipError_t launch_big_down(const GemmArgs& a, bool with_small, hipStream_t stream) {
+  return launch<false>(a, with_small, stream);
+}
 
 }  // namespace moe

@@ -76,8 +76,10 @@ hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_gate_up(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_down(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_big_down(const GemmArgs& a, hipStream_t stream);
+// Register-A / LDS-B grouped GEMMs over the big tiles (bf16 or 4-bit) and,
+// with with_small (4-bit only), the small tiles in the same launch.
+hipError_t launch_big_gate_up(const GemmArgs& a, bool with_small, hipStream_t stream);
+hipError_t launch_big_down(const GemmArgs& a, bool with_small, hipStream_t stream);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, uint16_t* xn, int T, int H, float eps, hipStream_t stream);
 

@@ -57,11 +57,15 @@ bool f32_intermediates(const moe_desc* d) { return d->w_dtype == MOE_F32 || d->w
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Big tiles (256 rows, LDS-staged, compute-bound kernel) for long prefill
+// Big tiles (128 rows, register-A / LDS-B kernel) for long prefill
 // chunks with bf16 or 4-bit weights; a host-side rule on T alone.
 bool big_tiles(const moe_desc* d, int32_t T) {
   return T >= moe::kBigTileMinTokens && (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_Q4B32);
 }
+
+// With big tiles on, the small tiles of 4-bit weights go through the
+// register-dequant kernel in the same launch as the big tiles.
+bool q4_small_reg(const moe_desc* d, int32_t T) { return d->w_dtype == MOE_Q4B32 && big_tiles(d, T); }
 
 moe_status check_weights(const moe_desc* d, const moe_weights* w) {
   if (!w || !ptr_ok(w->w)) return MOE_ERR_INVALID_ARG;
@@ -170,8 +174,9 @@ moe_status moe_grouped_gemm_gu(const moe_desc* d, int32_t T, const void* x, cons
   a.R = (int)rows(d, T);
   a.G = groups(d);
   a.big_on = big_tiles(d, T);
+  if (q4_small_reg(d, T)) return hip_status(moe::launch_big_gate_up(a, true, stream));
   if (a.big_on) {
-    const hipError_t e = moe::launch_big_gate_up(a, stream);
+    const hipError_t e = moe::launch_big_gate_up(a, false, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return hip_status(moe::launch_gate_up(a, stream));
@@ -209,8 +214,9 @@ moe_status moe_grouped_gemm_down(const moe_desc* d, int32_t T, const moe_weights
   a.R = R;
   a.G = groups(d);
   a.big_on = big_tiles(d, T);
+  if (q4_small_reg(d, T)) return hip_status(moe::launch_big_down(a, true, stream));
   if (a.big_on) {
-    const hipError_t e = moe::launch_big_down(a, stream);
+    const hipError_t e = moe::launch_big_down(a, false, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   return hip_status(moe::launch_down(a, stream));
