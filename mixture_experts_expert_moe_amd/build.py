@@ -17,6 +17,9 @@ LIB = os.path.join(PKG, "libmoe_gfx950.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["route.hip", "permute.hip", "gemm.hip", "gemm_big.hip", "combine.hip", "moe_api.cpp"]
+# Sources whose kernels issue their own vector loads (inline asm + explicit
+# vmcnt waits): their assembly is checked at build time.
+ASM_CHECKED = ["gemm_big.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -40,11 +43,28 @@ def _compile(src: str) -> str:
     return out
 
 
+def _check_asm(src: str) -> None:
+    from . import asm_check  # build-time only
+    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".s")
+    cmd = [HIPCC, *[f for f in FLAGS if f != "-fPIC"], "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc -S failed for %s:\n%s" % (src, r.stderr[-4000:]))
+    problems = asm_check.check_file(out)
+    if problems:
+        raise RuntimeError("assembly check failed for %s:\n%s" % (src, "\n".join(problems)))
+
+
 def build() -> str:
-    """Compile every HIP/C++ source for gfx950 and link the shared library."""
+    """Compile every HIP/C++ source for gfx950, check the assembly of the
+    kernels that manage their own loads, and link the shared library."""
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(ASM_CHECKED))) as ex:
+        objs_f = ex.map(_compile, SOURCES)
+        checks = [ex.submit(_check_asm, s) for s in ASM_CHECKED]
+        objs = list(objs_f)
+        for c in checks:
+            c.result()
     tmp = LIB + ".tmp"
     subprocess.check_call([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)
