@@ -116,29 +116,27 @@ class Runner:
         self.out = torch.empty((T, spec.hidden), dtype=odt, device="cuda")
 
     def step(self, i, ev=None):
-        """One layer: route, permute, gate/up, down, combine.  ev: optional list of
-        6 events recorded around the launches (same stream as the kernels)."""
+        """One layer: route + permute (one call), gate/up, down, combine.  ev:
+        optional list of 5 events recorded around the launches (same stream as
+        the kernels)."""
         moe, d, b, T = self.moe, self.desc, self.layer.bufs, self.T
         w = self.wsets[i % len(self.wsets)]
         gu, dn = self.structs[i % len(self.wsets)]
         x = self.x[i % len(self.x)]
         if ev:
             ev[0].record()
-        moe.moe_route_topk(d, T, x, w["w_router"], w.get("bias"), b)
+        moe.moe_route_permute(d, T, x, w["w_router"], w.get("bias"), b)
         if ev:
             ev[1].record()
-        moe.moe_permute(d, T, x, b)
-        if ev:
-            ev[2].record()
         moe.moe_grouped_gemm_gu(d, T, x, gu, b)
         if ev:
-            ev[3].record()
+            ev[2].record()
         moe.moe_grouped_gemm_down(d, T, dn, b)
         if ev:
-            ev[4].record()
+            ev[3].record()
         moe.moe_combine(d, T, None, self.out, b)
         if ev:
-            ev[5].record()
+            ev[4].record()
 
     def touched_groups(self):
         offs = self.layer.tensors["expert_offsets"][:4 * (self.spec.groups + 1)].view(self.torch.int32).cpu().numpy()
@@ -149,7 +147,7 @@ class Runner:
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)] if per_kernel else None
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)] if per_kernel else None
         # whole-step wall time without events first
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -163,7 +161,7 @@ class Runner:
             for i in range(steps):
                 self.step(warmup + steps + i, evs[i])
             torch.cuda.synchronize()
-            names = ["route", "permute", "gate_up", "down", "combine"]
+            names = ["route_permute", "gate_up", "down", "combine"]
             kms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
                    for j, n in enumerate(names)}
         return wall, U, kms

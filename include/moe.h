@@ -5,6 +5,7 @@
  *
  *   moe_route_topk        router logits, top-k experts and gates per token
  *   moe_permute           group (token, slot) pairs by expert + tile schedule
+ *   moe_route_permute     the two above in one call (two launches for a few tokens)
  *   moe_grouped_gemm_gu   one persistent launch: gate/up GEMM of every expert + SwiGLU
  *   moe_grouped_gemm_down one persistent launch: down GEMM of every expert
  *   moe_combine           gate-weighted, atomic-free sum of each token's rows
@@ -58,7 +59,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -113,7 +114,7 @@ typedef struct moe_weights {
 /* Caller-owned device buffers shared by the five calls of a layer.  Sizes in
  * bytes come from moe_buffer_sizes (index = position in this struct). */
 typedef struct moe_buffers {
-  float* logits;            /* [max_tokens][E] fp32 router logits */
+  float* logits;            /* [max_tokens][E] fp32 router logits, then scratch of moe_route_permute */
   int32_t* topk_ids;        /* [max_tokens][k] expert ids, descending logit */
   float* topk_w;            /* [max_tokens][k] gates */
   int32_t* expert_offsets;  /* [G+1] first row of each group; [G] = R */
@@ -157,6 +158,19 @@ moe_status moe_route_topk(const moe_desc* desc, int32_t T, const void* x, const 
  * Reads bufs->topk_ids. */
 moe_status moe_permute(const moe_desc* desc, int32_t T, const void* x, const moe_buffers* bufs,
                        hipStream_t stream);
+
+/* moe_route_topk followed by moe_permute, with the same arguments and the
+ * same results bit for bit (logits, topk_ids, topk_w, expert_offsets,
+ * row_token, token_row, the tile schedule, and x_q / x_scale for I8 weights).
+ * For T <= 16 (decode steps) it runs in two launches instead of four: the
+ * router logits are summed in fp64 over slices of H by many blocks (the
+ * partial sums go to the scratch that follows the logits in bufs->logits),
+ * then one block rounds them, selects the top-k, permutes and quantises.
+ * (fp64 sums in a different order round to the same fp32 logit except in
+ * cases that differ in the last fp64 bits exactly at an fp32 rounding
+ * boundary.)  For larger T it makes the two calls. */
+moe_status moe_route_permute(const moe_desc* desc, int32_t T, const void* x, const void* w_router,
+                             const float* bias, const moe_buffers* bufs, hipStream_t stream);
 
 /* Gate/up projection of every permuted row plus SwiGLU, all groups in one
  * persistent launch over the tile schedule:

@@ -72,6 +72,27 @@ struct CombineArgs {
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+// Routing + permutation of T <= kSmallRouteT tokens in two launches (fused
+// decode path): `slices` slices of H (H % (256 * slices) == 0), fp64 partials
+// [slices][T][E] in `partials`, int8 x quantisation when x_q is non-null.
+constexpr int kSmallRouteT = 16;
+constexpr int kRouteSlices = 8;
+struct RoutePermuteArgs {
+  RouteArgs r;
+  PermuteArgs p;
+  double* partials;
+  int slices;
+  int8_t* x_q;
+  float* x_scale;
+};
+hipError_t launch_route_partials(const RouteArgs& a, double* partials, int slices, hipStream_t stream);
+hipError_t launch_route_permute_small(const RoutePermuteArgs& a, hipStream_t stream);
+// Bytes of fp64 partials kept after the logits in the logits buffer (max_tokens tokens).
+inline size_t route_partials_bytes(int64_t max_tokens, int64_t E) {
+  return (size_t)kRouteSlices * (size_t)(max_tokens < kSmallRouteT ? max_tokens : kSmallRouteT) * (size_t)E * 8;
+}
+inline size_t route_partials_offset(int64_t max_tokens, int64_t E) { return ((size_t)max_tokens * E * 4 + 15) / 16 * 16; }
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_gate_up(const GemmArgs& a, hipStream_t stream);

@@ -100,7 +100,7 @@ moe_status moe_buffer_sizes(const moe_desc* d, size_t sizes[MOE_NUM_BUFFERS]) {
   const size_t G = E + S, Rmax = M * (k + S);
   const bool i8 = d->w_dtype == MOE_I8;
   const size_t fw = f32_intermediates(d) ? 4 : 2;
-  sizes[0] = M * E * 4;                                  // logits
+  sizes[0] = moe::route_partials_offset(M, E) + moe::route_partials_bytes(M, E);  // logits + fused-route scratch
   sizes[1] = M * k * 4;                                  // topk_ids
   sizes[2] = M * k * 4;                                  // topk_w
   sizes[3] = (G + 1) * 4;                                // expert_offsets
@@ -146,6 +146,36 @@ moe_status moe_permute(const moe_desc* d, int32_t T, const void* x, const moe_bu
   moe::PermuteArgs a{b->topk_ids, b->expert_offsets, b->row_token, b->token_row, b->sched, T, d->n_routed,
                      d->top_k, d->n_shared, big_tiles(d, T), (int)moe::sched_big_start(r_max, groups(d))};
   return hip_status(moe::launch_permute(a, stream));
+}
+
+moe_status moe_route_permute(const moe_desc* d, int32_t T, const void* x, const void* w_router, const float* bias,
+                             const moe_buffers* b, hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  const bool i8 = d->w_dtype == MOE_I8;
+  if (!ptr_ok(x) || !ptr_ok(w_router) || (bias && !aligned16(bias))) return MOE_ERR_INVALID_ARG;
+  if (!ptr_ok(b->logits) || !ptr_ok(b->topk_ids) || !ptr_ok(b->topk_w) || !ptr_ok(b->expert_offsets) ||
+      !ptr_ok(b->row_token) || !ptr_ok(b->token_row) || !ptr_ok(b->sched))
+    return MOE_ERR_INVALID_ARG;
+  if (i8 && (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale))) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (T > moe::kSmallRouteT) {
+    if ((s = moe_route_topk(d, T, x, w_router, bias, b, stream)) != MOE_OK) return s;
+    return moe_permute(d, T, x, b, stream);
+  }
+  int slices = moe::kRouteSlices;
+  while (d->hidden % (256 * slices) != 0) slices /= 2;
+  const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
+  moe::RoutePermuteArgs a{};
+  a.r = moe::RouteArgs{x, w_router, bias, b->logits, b->topk_ids, b->topk_w, T, d->hidden, d->n_routed, d->top_k,
+                       d->act_dtype == MOE_F32};
+  a.p = moe::PermuteArgs{b->topk_ids, b->expert_offsets, b->row_token, b->token_row, b->sched, T, d->n_routed,
+                         d->top_k, d->n_shared, false, (int)moe::sched_big_start(r_max, groups(d))};
+  a.partials = (double*)((char*)b->logits + moe::route_partials_offset(d->max_tokens, d->n_routed));
+  a.slices = slices;
+  a.x_q = i8 ? b->x_q : nullptr;
+  a.x_scale = i8 ? b->x_scale : nullptr;
+  return hip_status(moe::launch_route_permute_small(a, stream));
 }
 
 moe_status moe_grouped_gemm_gu(const moe_desc* d, int32_t T, const void* x, const moe_weights* w,

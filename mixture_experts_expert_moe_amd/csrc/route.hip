@@ -11,6 +11,7 @@
 // independent of how the sum is blocked.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "route_permute.hpp"
 
 namespace moe {
 namespace {
@@ -21,19 +22,23 @@ constexpr int kRouteWaves = 8;  // waves per block; each takes an eighth of H
 // holds token/expert (l % 16) and loads 8 consecutive h (one 16-byte load for
 // bf16, two for fp32) at h = base + 8 * (l / 16); MFMA step s of the 8 uses
 // element s, so A (x) and B (w_router) see the same permutation of K.
-template <bool kF32>
+// kPartial (T <= 16): block x takes slice x of H (gridDim.x slices) and
+// writes its fp64 partial sums, partials[slice][t][e], instead of logits.
+template <bool kF32, bool kPartial>
 __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const void* __restrict__ x,
                                                                         const void* __restrict__ wr,
                                                                         const float* __restrict__ bias,
-                                                                        float* __restrict__ logits, int T, int H,
+                                                                        float* __restrict__ logits,
+                                                                        double* __restrict__ partials, int T, int H,
                                                                         int E) {
   __shared__ double part[kRouteWaves][16][17];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int t0 = kPartial ? 0 : blockIdx.x * 16, e0 = blockIdx.y * 16;
   const int r = lane % 16, q = lane / 16;
   const int t = min(t0 + r, T - 1), e = min(e0 + r, E - 1);
-  const int hq = H / kRouteWaves;
-  const int hbeg = wave * hq;
+  const int hs = kPartial ? H / gridDim.x : H;  // this block's share of H
+  const int hq = hs / kRouteWaves;
+  const int hbeg = (kPartial ? blockIdx.x * hs : 0) + wave * hq;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};  // two independent MFMA chains
   // Batches of 8 steps of 32 h: all loads of a batch are issued before its MFMAs.
   constexpr int kNb = 8;
@@ -95,9 +100,13 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
         double s = part[0][tt][ee];
 #pragma unroll
         for (int w = 1; w < kRouteWaves; ++w) s += part[w][tt][ee];
-        float v = (float)s;
-        if (bias) v = __fadd_rn(v, bias[e0 + ee]);
-        logits[(size_t)(t0 + tt) * E + e0 + ee] = v;
+        if constexpr (kPartial) {
+          partials[((size_t)blockIdx.x * T + tt) * E + e0 + ee] = s;
+        } else {
+          float v = (float)s;
+          if (bias) v = __fadd_rn(v, bias[e0 + ee]);
+          logits[(size_t)(t0 + tt) * E + e0 + ee] = v;
+        }
       }
     }
   }
@@ -105,58 +114,13 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
 
 // One wave per token: k rounds of a wave arg-max (larger logit first, equal
 // logits -> lower expert id), then the softmax of the k selected logits in fp64.
+// One wave per token.
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                         int32_t* __restrict__ topk_ids,
                                                         float* __restrict__ topk_w, int T, int E, int k) {
-  const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= T) return;
-  constexpr int kPer = 4;  // E <= 256
-  float v[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + kWave * j;
-    v[j] = e < E ? logits[(size_t)t * E + e] : -INFINITY;
-  }
-  unsigned taken = 0;
-  float sel_v = 0.f;
-  int sel_id = 0;
-  for (int s = 0; s < k; ++s) {
-    // best remaining in this lane (lowest id among equals: ids grow with j)
-    float bv = -INFINITY;
-    int bid = 0x7fffffff;
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + kWave * j;
-      if (e < E && !(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bid))) {
-        bv = v[j];
-        bid = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oid = __shfl_xor(bid, o, kWave);
-      if (ov > bv || (ov == bv && oid < bid)) {
-        bv = ov;
-        bid = oid;
-      }
-    }
-    if ((bid % kWave) == lane) taken |= 1u << (bid / kWave);
-    if (lane == s) {
-      sel_v = bv;
-      sel_id = bid;
-    }
-  }
-  // Gates: softmax over the selected logits, fp64, slot order, rounded once.
-  const double top = (double)__shfl(sel_v, 0, kWave);
-  const double ex = lane < k ? exp((double)sel_v - top) : 0.0;
-  double den = 0.0;
-  for (int s = 0; s < k; ++s) den += __shfl(ex, s, kWave);
-  if (lane < k) {
-    topk_ids[(size_t)t * k + lane] = sel_id;
-    topk_w[(size_t)t * k + lane] = (float)(ex / den);
-  }
+  topk_wave(logits + (size_t)t * E, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, nullptr);
 }
 
 }  // namespace
@@ -164,15 +128,26 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   dim3 grid((a.T + 15) / 16, (a.E + 15) / 16);
   if (a.act_f32)
-    hipLaunchKernelGGL(route_logits_kernel<true>, grid, dim3(kWave * kRouteWaves), 0, stream, a.x, a.w_router,
-                       a.bias, a.logits, a.T, a.H, a.E);
+    hipLaunchKernelGGL((route_logits_kernel<true, false>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+                       a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
   else
-    hipLaunchKernelGGL(route_logits_kernel<false>, grid, dim3(kWave * kRouteWaves), 0, stream, a.x, a.w_router,
-                       a.bias, a.logits, a.T, a.H, a.E);
+    hipLaunchKernelGGL((route_logits_kernel<false, false>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+                       a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, a.topk_ids, a.topk_w,
                      a.T, a.E, a.k);
+  return hipGetLastError();
+}
+
+hipError_t launch_route_partials(const RouteArgs& a, double* partials, int slices, hipStream_t stream) {
+  dim3 grid(slices, (a.E + 15) / 16);
+  if (a.act_f32)
+    hipLaunchKernelGGL((route_logits_kernel<true, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+                       a.w_router, nullptr, nullptr, partials, a.T, a.H, a.E);
+  else
+    hipLaunchKernelGGL((route_logits_kernel<false, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+                       a.w_router, nullptr, nullptr, partials, a.T, a.H, a.E);
   return hipGetLastError();
 }
 

@@ -1,0 +1,376 @@
+// Device functions shared by the routing and permutation kernels: the top-k
+// of one token by one wave, the permutation by one block and the int8
+// quantisation of one row by one block.  The stand-alone kernels and the
+// fused small-T routing kernel call the same code, so their results agree
+// bit for bit.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kMaxGroups = 257;
+
+// Exclusive wave-wide prefix sum (64 lanes), returns the lane's exclusive sum; *total = sum of all lanes.
+__device__ __forceinline__ int wave_excl_scan(int v, int* total) {
+  const int lane = threadIdx.x % kWave;
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int n = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += n;
+  }
+  *total = __shfl(inc, kWave - 1, kWave);
+  return inc - v;
+}
+
+// Top-k of one token by one wave: k rounds of a wave arg-max (larger logit
+// first, equal logits -> lower expert id), then the softmax of the k selected
+// logits in fp64, summed in slot order, rounded once.  `row` holds the
+// token's E logits (global or shared memory); ids/w receive k entries (and
+// ids_copy, if non-null).
+__device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* ids, float* w,
+                                          int32_t* ids_copy) {
+  const int lane = threadIdx.x % kWave;
+  constexpr int kPer = 4;  // E <= 256
+  float v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    v[j] = e < E ? row[e] : -INFINITY;
+  }
+  unsigned taken = 0;
+  float sel_v = 0.f;
+  int sel_id = 0;
+  for (int s = 0; s < k; ++s) {
+    // best remaining in this lane (lowest id among equals: ids grow with j)
+    float bv = -INFINITY;
+    int bid = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int e = lane + kWave * j;
+      if (e < E && !(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bid))) {
+        bv = v[j];
+        bid = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, kWave);
+      const int oid = __shfl_xor(bid, o, kWave);
+      if (ov > bv || (ov == bv && oid < bid)) {
+        bv = ov;
+        bid = oid;
+      }
+    }
+    if ((bid % kWave) == lane) taken |= 1u << (bid / kWave);
+    if (lane == s) {
+      sel_v = bv;
+      sel_id = bid;
+    }
+  }
+  // Gates: softmax over the selected logits, fp64, slot order, rounded once.
+  const double top = (double)__shfl(sel_v, 0, kWave);
+  const double ex = lane < k ? exp((double)sel_v - top) : 0.0;
+  double den = 0.0;
+  for (int s = 0; s < k; ++s) den += __shfl(ex, s, kWave);
+  if (lane < k) {
+    ids[lane] = sel_id;
+    w[lane] = (float)(ex / den);
+    if (ids_copy) ids_copy[lane] = sel_id;
+  }
+}
+
+// Row `row` of src by one block of NT threads: s = max|v| / 127 (IEEE
+// division), q = clamp(rne(v / s), -127, 127); s = 0 gives q = 0.  The block
+// may call this for several rows in turn.
+template <int NT>
+__device__ __forceinline__ void quant_row_block(const void* __restrict__ src, bool src_f32, int8_t* __restrict__ q,
+                                                float* __restrict__ scale, int row, int cols) {
+  __shared__ float s_max[NT / kWave];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  auto load = [&](int c) -> float {
+    return src_f32 ? ((const float*)src)[(size_t)row * cols + c]
+                   : bf16_bits_to_f32(((const uint16_t*)src)[(size_t)row * cols + c]);
+  };
+  float amax = 0.f;
+  for (int c = threadIdx.x; c < cols; c += NT) amax = fmaxf(amax, fabsf(load(c)));
+  amax = wave_max(amax);
+  if (lane == 0) s_max[wave] = amax;
+  __syncthreads();
+  amax = s_max[0];
+#pragma unroll
+  for (int w = 1; w < NT / kWave; ++w) amax = fmaxf(amax, s_max[w]);
+  const float s = __fdiv_rn(amax, 127.0f);
+  if (threadIdx.x == 0) scale[row] = s;
+  for (int c = threadIdx.x; c < cols; c += NT) {
+    float r = 0.f;
+    if (s != 0.f) r = fminf(127.f, fmaxf(-127.f, rintf(__fdiv_rn(load(c), s))));
+    q[(size_t)row * cols + c] = (int8_t)r;
+  }
+  __syncthreads();  // s_max is reused by the next row
+}
+
+// Row `row` of src by one wave (the same arithmetic as quant_row_block):
+// 16-byte loads of 8 (bf16) or 4 (fp32) values per lane; for a row of at
+// most 2048 values the row stays in registers between the two passes.
+__device__ __forceinline__ float q_to_int(float v, float s) {
+  return s != 0.f ? fminf(127.f, fmaxf(-127.f, rintf(__fdiv_rn(v, s)))) : 0.f;
+}
+template <bool kF32>
+__device__ __forceinline__ void quant_row_wave_t(const void* __restrict__ src, int8_t* __restrict__ q,
+                                                 float* __restrict__ scale, int row, int cols) {
+  constexpr int V = kF32 ? 4 : 8;  // values per 16-byte load
+  constexpr int kRegs = 2048 / (kWave * V);  // loads per lane kept in registers
+  const int lane = threadIdx.x % kWave;
+  const uint8_t* base = (const uint8_t*)src + (size_t)row * cols * (kF32 ? 4 : 2);
+  auto val = [&](const u32x4& u, int i) -> float {
+    return kF32 ? __uint_as_float(u[i]) : bf16_bits_to_f32(i % 2 ? (u[i / 2] >> 16) : (u[i / 2] & 0xffffu));
+  };
+  const bool in_regs = cols <= 2048;
+  u32x4 keep[kRegs];
+  float amax = 0.f;
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+      const int c = (j * kWave + lane) * V;
+      keep[j] = c < cols ? ld16(base + (size_t)c * (kF32 ? 4 : 2)) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j)
+#pragma unroll
+      for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(keep[j], i)));
+  } else {
+    for (int c = lane * V; c < cols; c += kWave * V) {
+      const u32x4 u = ld16(base + (size_t)c * (kF32 ? 4 : 2));
+#pragma unroll
+      for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(u, i)));
+    }
+  }
+  amax = wave_max(amax);
+  const float s = __fdiv_rn(amax, 127.0f);
+  if (lane == 0) scale[row] = s;
+  auto put = [&](const u32x4& u, int c) {
+    uint32_t packed[V / 4];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t b = (uint32_t)(uint8_t)(int8_t)q_to_int(val(u, i), s);
+      if (i % 4 == 0) packed[i / 4] = b; else packed[i / 4] |= b << (8 * (i % 4));
+    }
+    if constexpr (V == 8) *reinterpret_cast<u32x2*>(q + (size_t)row * cols + c) = u32x2{packed[0], packed[1]};
+    else *reinterpret_cast<uint32_t*>(q + (size_t)row * cols + c) = packed[0];
+  };
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kRegs; ++j) {
+      const int c = (j * kWave + lane) * V;
+      if (c < cols) put(keep[j], c);
+    }
+  } else {
+    for (int c = lane * V; c < cols; c += kWave * V) put(ld16(base + (size_t)c * (kF32 ? 4 : 2)), c);
+  }
+}
+__device__ __forceinline__ void quant_row_wave(const void* __restrict__ src, bool src_f32, int8_t* __restrict__ q,
+                                               float* __restrict__ scale, int row, int cols) {
+  if (src_f32) quant_row_wave_t<true>(src, q, scale, row, cols);
+  else quant_row_wave_t<false>(src, q, scale, row, cols);
+}
+
+// The permutation by one block of kPermThreads threads (all in LDS; `lds` is
+// permute_lds_bytes(T, E) bytes of shared memory).  topk_ids may point to
+// global or shared memory.
+__device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* __restrict__ offsets,
+                                              int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
+                                              int32_t* __restrict__ sched, int T, int E, int k, int S, int big_on,
+                                              int big_start, uint32_t* lds) {
+  const int W = (T + 31) / 32;                       // 32-token words per expert
+  uint32_t* bits = lds;                              // [E][W]
+  uint16_t* pre = (uint16_t*)(lds + (size_t)E * W);  // [E][W] exclusive popcount prefix
+  __shared__ int32_t s_off[kMaxGroups + 1];
+  __shared__ int32_t s_tile[kMaxGroups + 1];
+  __shared__ int32_t s_cnt[kMaxGroups];
+  const int G = E + S;
+  const int kS = k + S;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int pairs = T * k;
+
+  for (int i = threadIdx.x; i < E * W; i += kPermThreads) bits[i] = 0u;
+  __syncthreads();
+  // 1. bitmap
+  for (int i = threadIdx.x; i < pairs; i += kPermThreads) {
+    const int e = topk_ids[i], t = i / k;
+    if ((unsigned)e < (unsigned)E) atomicOr(&bits[e * W + t / 32], 1u << (t % 32));
+  }
+  __syncthreads();
+  // 2. per-expert prefix over words (a single word: prefix 0, count = popcount)
+  if (W == 1) {
+    for (int e = threadIdx.x; e < E; e += kPermThreads) {
+      pre[e] = 0;
+      s_cnt[e] = __popc(bits[e]);
+    }
+  } else for (int e = wave; e < E; e += kPermWaves) {
+    int base = 0;
+    for (int w0 = 0; w0 < W; w0 += kWave) {
+      const int w = w0 + lane;
+      const int c = w < W ? __popc(bits[e * W + w]) : 0;
+      int tot;
+      const int ex = wave_excl_scan(c, &tot);
+      if (w < W) pre[e * W + w] = (uint16_t)(base + ex);
+      base += tot;
+    }
+    if (lane == 0) s_cnt[e] = base;
+  }
+  if (S && threadIdx.x == 0) s_cnt[E] = T;
+  __syncthreads();
+  // 3. offsets over groups, then the two tile lists (wave 0 scans; each lane
+  //    takes 5 consecutive groups).  With big tiles on, a group of >= 128 rows
+  //    is cut into tiles of 128 rows (a remainder of >= 64 rows is one more,
+  //    partial, big tile; a smaller remainder goes to small tiles).  Small
+  //    tiles hold <= 64 rows: all full ones first (by group), then the partial
+  //    ones by descending height (ties by group) -- heavy tiles first.
+  __shared__ int32_t s_hist[kTileRows];  // partial small tiles per height, then start slot per height
+  __shared__ int32_t s_small[kMaxGroups];      // rows of g handled by small tiles (the last rows of g)
+  __shared__ int32_t s_big[kMaxGroups + 1];    // first big tile of g
+  if (threadIdx.x < kTileRows) s_hist[threadIdx.x] = 0;
+  __syncthreads();
+  if (wave == 0) {
+    constexpr int kPer = (kMaxGroups + kWave - 1) / kWave;
+    int rows_sum = 0, full_sum = 0, big_sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int g = lane * kPer + i;
+      const int n = g < G ? s_cnt[g] : 0;
+      int nbig = 0, nsmall = n;
+      if (big_on && n >= kBigTileMin) {
+        nbig = n / kBigTileRows + (n % kBigTileRows >= kBigPartMin ? 1 : 0);
+        nsmall = n % kBigTileRows >= kBigPartMin ? 0 : n % kBigTileRows;
+      }
+      rows_sum += n;
+      full_sum += nsmall / kTileRows;
+      big_sum += nbig;
+    }
+    int rows_tot, full_tot, big_tot;
+    int r = wave_excl_scan(rows_sum, &rows_tot);
+    int f = wave_excl_scan(full_sum, &full_tot);
+    int b = wave_excl_scan(big_sum, &big_tot);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int g = lane * kPer + i;
+      if (g < G) {
+        const int n = s_cnt[g];
+        int nbig = 0, nsmall = n;
+        if (big_on && n >= kBigTileMin) {
+          nbig = n / kBigTileRows + (n % kBigTileRows >= kBigPartMin ? 1 : 0);
+          nsmall = n % kBigTileRows >= kBigPartMin ? 0 : n % kBigTileRows;
+        }
+        s_off[g] = r;
+        s_tile[g] = f;  // first full small tile of g
+        s_big[g] = b;
+        s_small[g] = nsmall;
+        r += n;
+        f += nsmall / kTileRows;
+        b += nbig;
+        if (nsmall % kTileRows) atomicAdd(&s_hist[nsmall % kTileRows], 1);
+      }
+    }
+    if (lane == 0) {
+      s_off[G] = rows_tot;
+      s_tile[G] = full_tot;
+      s_big[G] = big_tot;
+    }
+  }
+  __syncthreads();
+  __shared__ int32_t s_rank[kMaxGroups];  // rank of g's partial tile among the partial tiles of its height
+  if (wave == 0) {
+    // start slot of each partial height, tallest first: lane l takes height 63 - l
+    static_assert(kTileRows == kWave, "one lane per tile height");
+    const int h = kTileRows - 1 - lane;
+    const int c = h >= 1 ? s_hist[h] : 0;
+    int total;
+    const int ex = wave_excl_scan(c, &total);
+    if (h >= 1) s_hist[h] = s_tile[G] + ex;
+    if (lane == 0) s_hist[0] = s_tile[G] + total;  // total small tiles (lane 0 read height 63 already)
+  } else if (wave == 1) {
+    // ranks: groups in chunks of 64 (one per lane).  Lanes holding the same
+    // height are found with one ballot per height bit; rank = lower such
+    // lanes + the chunks before (a running count per height).
+    __shared__ int32_t s_run[kTileRows];
+    s_run[lane] = 0;
+    for (int c0 = 0; c0 < G; c0 += kWave) {
+      const int g = c0 + lane;
+      const int rem = g < G ? s_small[g] % kTileRows : 0;
+      uint64_t same = ~0ull;
+#pragma unroll
+      for (int bit = 0; bit < 6; ++bit) {
+        const uint64_t m = __ballot((rem >> bit) & 1);
+        same &= ((rem >> bit) & 1) ? m : ~m;
+      }
+      const int r = __popcll(same & ((1ull << lane) - 1ull));
+      const int base = rem ? s_run[rem] : 0;
+      __builtin_amdgcn_wave_barrier();
+      // the highest lane of each height adds the chunk's count
+      if (rem && (same >> lane) == 1ull) s_run[rem] = base + r + 1;
+      __builtin_amdgcn_wave_barrier();
+      if (g < G) s_rank[g] = base + r;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < kSchedHeader; i += kPermThreads)
+    sched[i] = i == kSchedSmall ? s_hist[0] : i == kSchedGroups ? G : i == kSchedRows ? s_off[G]
+             : i == kSchedBig ? s_big[G] : i == kSchedBigStart ? big_start : 0;
+  for (int g = threadIdx.x; g <= G; g += kPermThreads) offsets[g] = s_off[g];
+  for (int g = threadIdx.x; g < G; g += kPermThreads) {
+    const int n = s_off[g + 1] - s_off[g];
+    const int nsmall = s_small[g];
+    const int big_rows = n - nsmall;
+    // big tiles of g: rows [s_off[g], s_off[g] + big_rows) in pieces of 128 (last one partial)
+    int32_t* bdst = sched + big_start + (size_t)s_big[g] * kTileInts;
+    for (int i = 0; i * kBigTileRows < big_rows; ++i) {
+      bdst[i * kTileInts + 0] = g;
+      bdst[i * kTileInts + 1] = s_off[g] + i * kBigTileRows;
+      bdst[i * kTileInts + 2] = min(kBigTileRows, big_rows - i * kBigTileRows);
+      bdst[i * kTileInts + 3] = 0;
+    }
+    // small tiles of g: the remaining rows
+    const int row_base = s_off[g] + big_rows;
+    const int full = nsmall / kTileRows, rem = nsmall % kTileRows;
+    int32_t* dst = sched + kSchedHeader + (size_t)s_tile[g] * kTileInts;
+    for (int i = 0; i < full; ++i) {
+      dst[i * kTileInts + 0] = g;
+      dst[i * kTileInts + 1] = row_base + i * kTileRows;
+      dst[i * kTileInts + 2] = kTileRows;
+      dst[i * kTileInts + 3] = 0;
+    }
+    if (rem) {
+      // partial tiles of one height in group order
+      int32_t* t = sched + kSchedHeader + (size_t)(s_hist[rem] + s_rank[g]) * kTileInts;
+      t[0] = g;
+      t[1] = row_base + full * kTileRows;
+      t[2] = rem;
+      t[3] = 0;
+    }
+  }
+  // 4. rows
+  for (int i = threadIdx.x; i < pairs; i += kPermThreads) {
+    const int e = topk_ids[i], t = i / k, j = i % k;
+    int row = -1;
+    if ((unsigned)e < (unsigned)E) {
+      const int w = e * W + t / 32;
+      row = s_off[e] + pre[w] + __popc(bits[w] & ((1u << (t % 32)) - 1u));
+      row_token[row] = t;
+    }
+    token_row[(size_t)t * kS + j] = row;
+  }
+  if (S) {
+    for (int t = threadIdx.x; t < T; t += kPermThreads) {
+      const int row = s_off[E] + t;
+      token_row[(size_t)t * kS + k] = row;
+      row_token[row] = t;
+    }
+  }
+}
+
+}  // namespace moe

@@ -19,8 +19,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
           -4: "MOE_ERR_HIP"}
 
 # The C-ABI entry points declared in include/moe.h.
-EXPORTS = ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_grouped_gemm_gu", "moe_grouped_gemm_down",
-           "moe_combine", "moe_rmsnorm", "moe_status_string", "moe_abi_version")
+EXPORTS = ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
+           "moe_grouped_gemm_down", "moe_combine", "moe_rmsnorm", "moe_status_string", "moe_abi_version")
 
 
 class MoeDesc(ctypes.Structure):
@@ -60,6 +60,7 @@ def lib():
         L.moe_buffer_sizes.argtypes = [P(MoeDesc), P(ctypes.c_size_t)]
         L.moe_route_topk.argtypes = [P(MoeDesc), i32, vp, vp, vp, P(MoeBuffers), vp]
         L.moe_permute.argtypes = [P(MoeDesc), i32, vp, P(MoeBuffers), vp]
+        L.moe_route_permute.argtypes = [P(MoeDesc), i32, vp, vp, vp, P(MoeBuffers), vp]
         L.moe_grouped_gemm_gu.argtypes = [P(MoeDesc), i32, vp, P(MoeWeights), P(MoeBuffers), vp]
         L.moe_grouped_gemm_down.argtypes = [P(MoeDesc), i32, P(MoeWeights), P(MoeBuffers), vp]
         L.moe_combine.argtypes = [P(MoeDesc), i32, vp, vp, P(MoeBuffers), vp]
@@ -67,7 +68,7 @@ def lib():
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
-        for f in ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_grouped_gemm_gu",
+        for f in ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
                   "moe_grouped_gemm_down", "moe_combine", "moe_rmsnorm"):
             getattr(L, f).restype = i32
         _lib = L
@@ -133,6 +134,11 @@ def moe_permute(desc, T, x, bufs: MoeBuffers, stream=None):
     _check("moe_permute", lib().moe_permute(ctypes.byref(desc), T, _ptr(x), ctypes.byref(bufs), _stream(stream)))
 
 
+def moe_route_permute(desc, T, x, w_router, bias, bufs: MoeBuffers, stream=None):
+    _check("moe_route_permute", lib().moe_route_permute(ctypes.byref(desc), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                                        ctypes.byref(bufs), _stream(stream)))
+
+
 def moe_grouped_gemm_gu(desc, T, x, w_gu: MoeWeights, bufs: MoeBuffers, stream=None):
     _check("moe_grouped_gemm_gu", lib().moe_grouped_gemm_gu(ctypes.byref(desc), T, _ptr(x), ctypes.byref(w_gu),
                                                             ctypes.byref(bufs), _stream(stream)))
@@ -176,8 +182,7 @@ class MoeLayer:
         """The five calls of the layer on one stream; out receives [T][H]."""
         T = x.shape[0]
         d = self.desc
-        moe_route_topk(d, T, x, self.w["w_router"], self.w.get("bias"), self.bufs, stream)
-        moe_permute(d, T, x, self.bufs, stream)
+        moe_route_permute(d, T, x, self.w["w_router"], self.w.get("bias"), self.bufs, stream)
         moe_grouped_gemm_gu(d, T, x, self.gu, self.bufs, stream)
         moe_grouped_gemm_down(d, T, self.dn, self.bufs, stream)
         moe_combine(d, T, residual, out, self.bufs, stream)
@@ -214,8 +219,7 @@ class MoeStack:
         d, b, w = self.desc, self.bufs, self.layers[l]
         xn = self.xn[:T]
         moe_rmsnorm(T, d.hidden, self.eps, x, xn, stream)
-        moe_route_topk(d, T, xn, w["w_router"], w.get("bias"), b, stream)
-        moe_permute(d, T, xn, b, stream)
+        moe_route_permute(d, T, xn, w["w_router"], w.get("bias"), b, stream)
         moe_grouped_gemm_gu(d, T, xn, self.gu[l], b, stream)
         moe_grouped_gemm_down(d, T, self.dn[l], b, stream)
         moe_combine(d, T, x, out, b, stream)

@@ -123,6 +123,11 @@ class GpuLayer:
         from mixture_experts_expert_moe_amd import moe
         moe.moe_permute(self.desc, self.T, self.x, self.layer.bufs)
 
+    def route_permute(self):
+        from mixture_experts_expert_moe_amd import moe
+        moe.moe_route_permute(self.desc, self.T, self.x, self.layer.w["w_router"], self.layer.w.get("bias"),
+                              self.layer.bufs)
+
     def gate_up(self):
         from mixture_experts_expert_moe_amd import moe
         moe.moe_grouped_gemm_gu(self.desc, self.T, self.x, self.layer.gu, self.layer.bufs)

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 1
+    assert L.moe_abi_version() == 2
 
 
 def test_status_strings():
@@ -54,7 +54,9 @@ def status(fn, *args):
 def test_buffer_sizes_match_shapes():
     s = moe.moe_buffer_sizes(desc())
     R = 256 * 9
-    assert s["logits"] == 256 * 128 * 4
+    # fp32 logits, then 8 H-slices x min(max_tokens, 16) tokens x E of fp64 partial sums (few-token routing)
+    assert s["logits"] == 256 * 128 * 4 + 8 * 16 * 128 * 8
+    assert moe.moe_buffer_sizes(desc(max_tokens=3))["logits"] == 3 * 128 * 4 + 8 * 3 * 128 * 8
     assert s["topk_ids"] == s["topk_w"] == 256 * 8 * 4
     assert s["expert_offsets"] == 130 * 4
     assert s["row_token"] == R * 4 and s["token_row"] == 256 * 9 * 4
@@ -84,6 +86,7 @@ def test_calls_reject_before_launch():
     # T > max_tokens
     assert status("moe_route_topk", by(d), 257, FAKE, FAKE, None, by(b), None) == -3
     assert status("moe_permute", by(d), 300, FAKE, by(b), None) == -3
+    assert status("moe_route_permute", by(d), 257, FAKE, FAKE, None, by(b), None) == -3
     assert status("moe_grouped_gemm_gu", by(d), 257, FAKE, by(w), by(b), None) == -3
     assert status("moe_grouped_gemm_down", by(d), 257, by(w), by(b), None) == -3
     assert status("moe_combine", by(d), 257, None, FAKE, by(b), None) == -3
@@ -91,6 +94,10 @@ def test_calls_reject_before_launch():
     assert status("moe_route_topk", by(d), -1, FAKE, FAKE, None, by(b), None) == -1
     assert status("moe_route_topk", by(d), 4, None, FAKE, None, by(b), None) == -1
     assert status("moe_route_topk", by(d), 4, FAKE + 2, FAKE, None, by(b), None) == -1
+    assert status("moe_route_permute", by(d), 4, None, FAKE, None, by(b), None) == -1
+    assert status("moe_route_permute", by(d), 4, FAKE, FAKE, FAKE + 4, by(b), None) == -1   # misaligned bias
+    assert status("moe_route_permute", by(desc(wt="i8")), 4, FAKE, FAKE, None, by(moe.MoeBuffers(
+        *[None if n in ("x_q", "x_scale") else FAKE for n in moe.BUFFER_NAMES])), None) == -1  # int8 needs x_q
     assert status("moe_grouped_gemm_gu", by(d), 4, FAKE, by(moe.MoeWeights(None, None, None)), by(b), None) == -1
     d8 = desc(wt="i8")
     assert status("moe_grouped_gemm_gu", by(d8), 4, FAKE, by(w), by(b), None) == -1       # no scales
@@ -112,6 +119,7 @@ def test_zero_tokens_returns_ok_without_launch():
     by = ctypes.byref
     assert status("moe_route_topk", by(d), 0, FAKE, FAKE, None, by(b), None) == 0
     assert status("moe_permute", by(d), 0, FAKE, by(b), None) == 0
+    assert status("moe_route_permute", by(d), 0, FAKE, FAKE, None, by(b), None) == 0
     assert status("moe_grouped_gemm_gu", by(d), 0, FAKE, by(w), by(b), None) == 0
     assert status("moe_grouped_gemm_down", by(d), 0, by(w), by(b), None) == 0
     assert status("moe_combine", by(d), 0, None, FAKE, by(b), None) == 0

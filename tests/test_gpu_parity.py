@@ -245,3 +245,59 @@ def test_deterministic_and_chunk_invariant():
     g2 = gh.GpuLayer(part)
     g2.run()
     np.testing.assert_array_equal(g2.output(), a[30:41])
+
+
+# moe_route_permute: two launches for T <= 16 (H-sliced fp64 partial logits,
+# then one block for top-k, permutation and int8 quantisation), the two
+# separate calls above that.  Same results bit for bit as moe_route_topk +
+# moe_permute, and the oracle's routing and permutation.
+FUSED_ROUTE = [
+    ("bf16_e128k8s1_t1", 2048, 512, 128, 8, 1, 1, "bf16", 0.0),
+    ("bf16_e128k8s1_t2", 2048, 512, 128, 8, 1, 2, "bf16", 0.0),
+    ("bf16_e128k8s1_t5", 2048, 512, 128, 8, 1, 5, "bf16", 0.0),
+    ("bf16_e128k8s1_t16", 2048, 512, 128, 8, 1, 16, "bf16", 0.0),
+    ("bf16_e128k8s1_t17_unfused", 2048, 512, 128, 8, 1, 17, "bf16", 0.0),
+    ("i8_e128k8s1_t1", 2048, 512, 128, 8, 1, 1, "i8", 0.0),
+    ("i8_e128k8s1_t8", 2048, 512, 128, 8, 1, 8, "i8", 0.0),
+    ("f32_e16k2_t16", 2048, 512, 16, 2, 0, 16, "f32", 0.0),
+    ("q4_e16k4s1_t4_zipf", 512, 256, 16, 4, 1, 4, "q4", 1.1),
+    ("bf16_e8k8s1_t3_h256", 256, 256, 8, 8, 1, 3, "bf16", 0.0),
+    ("bf16_e256k16_t16", 1024, 256, 256, 16, 0, 16, "bf16", 0.0),
+]
+
+ROUTE_PERMUTE_BUFFERS = ("topk_ids", "topk_w", "expert_offsets", "row_token", "token_row", "sched", "x_q", "x_scale")
+
+
+@pytest.mark.parametrize("case", FUSED_ROUTE, ids=[c[0] for c in FUSED_ROUTE])
+def test_route_permute_matches_separate_calls(case):
+    torch = gh.torch_mod()
+    name, H, I, E, k, S, T, wt, zipf = case
+    d = case_inputs(H, I, E, k, S, T, wt, zipf, seed=11)
+    spec = d["spec"]
+    say("case", name, "T", T)
+    g = gh.GpuLayer(d)
+    g.route()
+    g.permute()
+    torch.cuda.synchronize()
+    ref = {n: g.layer.tensors[n].clone() for n in ROUTE_PERMUTE_BUFFERS if g.layer.tensors.get(n) is not None}
+    for n in list(ref) + ["logits"]:
+        g.layer.tensors[n].fill_(0x5a)
+    g.route_permute()
+    torch.cuda.synchronize()
+    # routing against the oracle (logits bit for bit, ids, gates within an ulp)
+    ref_route = oracle.route(d["x"], d["w_router"], spec.top_k, d.get("bias"))
+    check_route(g, d, ref_route)
+    check_permute(g, oracle.permute(ref_route[1], spec.n_routed, spec.n_shared))
+    # every other buffer the two calls write, bit for bit (only the bytes the calls define)
+    nbytes = dict(topk_ids=T * k * 4, topk_w=T * k * 4, expert_offsets=(E + S + 1) * 4, row_token=T * (k + S) * 4,
+                  token_row=T * (k + S) * 4, x_q=T * H, x_scale=T * 4)
+    head, small, big = g.sched()
+    nbytes["sched"] = (32 + 4 * len(small)) * 4
+    for n, t in ref.items():
+        a = t.view(torch.uint8)[:nbytes[n]].cpu().numpy()
+        b = g.layer.tensors[n].view(torch.uint8)[:nbytes[n]].cpu().numpy()
+        np.testing.assert_array_equal(b, a, err_msg="%s: fused differs from moe_route_topk + moe_permute" % n)
+    if wt == "i8":
+        xq, xs = oracle.quantize_x(spec, d["x"])
+        np.testing.assert_array_equal(gh.buf(g.layer, "x_q", np.int8, (T, H)), xq)
+        np.testing.assert_array_equal(gh.buf(g.layer, "x_scale", np.float32, (T,)), xs)
