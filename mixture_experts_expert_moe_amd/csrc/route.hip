@@ -118,9 +118,13 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
                                                         int32_t* __restrict__ topk_ids,
                                                         float* __restrict__ topk_w, int T, int E, int k) {
-  const int t = blockIdx.x * 4 + threadIdx.x / kWave;
+  __shared__ long long s_key[4][kTopkKeys];
+  __shared__ float s_sel[4][16];
+  const int wave = threadIdx.x / kWave;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  topk_wave(logits + (size_t)t * E, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, nullptr);
+  topk_wave(logits + (size_t)t * E, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, nullptr, s_key[wave],
+            s_sel[wave]);
 }
 
 }  // namespace

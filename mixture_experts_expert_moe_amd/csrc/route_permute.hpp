@@ -14,74 +14,125 @@ constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
 constexpr int kMaxGroups = 257;
 
-// Exclusive wave-wide prefix sum (64 lanes), returns the lane's exclusive sum; *total = sum of all lanes.
+// Wave-wide (64-lane) scans and reductions with DPP lane moves, which stay in
+// the VALU instead of a round trip through the LDS crossbar per step: row
+// shifts by 1, 2, 4, 8 within each 16-lane row, then the row broadcasts of
+// lanes 15 and 31 (the gfx9 wave-scan pattern).  Every lane of the wave must
+// be active.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, kCtrl, kRowMask, 0xf, false);
+}
+constexpr int kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118;
+constexpr int kDppBcast15 = 0x142, kDppBcast31 = 0x143;
+
+// Inclusive prefix sum over the wave (lanes that read past the start of a
+// row or of the wave add 0).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp_i32<kDppShr1, 0xf>(0, v);
+  v += dpp_i32<kDppShr2, 0xf>(0, v);
+  v += dpp_i32<kDppShr4, 0xf>(0, v);
+  v += dpp_i32<kDppShr8, 0xf>(0, v);
+  v += dpp_i32<kDppBcast15, 0xa>(0, v);
+  v += dpp_i32<kDppBcast31, 0xc>(0, v);
+  return v;
+}
+
+// Exclusive wave-wide prefix sum, returns the lane's exclusive sum; *total = sum of all lanes.
 __device__ __forceinline__ int wave_excl_scan(int v, int* total) {
-  const int lane = threadIdx.x % kWave;
-  int inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int n = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += n;
-  }
-  *total = __shfl(inc, kWave - 1, kWave);
+  const int inc = wave_incl_scan(v);
+  *total = __builtin_amdgcn_readlane(inc, kWave - 1);
   return inc - v;
 }
 
-// Top-k of one token by one wave: k rounds of a wave arg-max (larger logit
-// first, equal logits -> lower expert id), then the softmax of the k selected
-// logits in fp64, summed in slot order, rounded once.  `row` holds the
-// token's E logits (global or shared memory); ids/w receive k entries (and
-// ids_copy, if non-null).
-__device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* ids, float* w,
-                                          int32_t* ids_copy) {
+// Maximum over the wave (max is exact, so the combining order does not
+// matter).  Lanes that read past the start of a row keep their own value.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  int b = __float_as_int(v);
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_i32<kDppShr1, 0xf>(b, b))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_i32<kDppShr2, 0xf>(b, b))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_i32<kDppShr4, 0xf>(b, b))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_i32<kDppShr8, 0xf>(b, b))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_i32<kDppBcast15, 0xa>(b, b))));
+  b = __float_as_int(fmaxf(__int_as_float(b), __int_as_float(dpp_i32<kDppBcast31, 0xc>(b, b))));
+  return __int_as_float(__builtin_amdgcn_readlane(b, kWave - 1));
+}
+
+// Orders LDS writes of this wave before its later LDS reads by other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(b & 0xffffffffll), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(b >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
+// Top-k of one token by one wave.  Every (logit, id) pair gets a 64-bit key
+// that orders larger logits first and, among equal logits, the lower expert
+// id first (+0 and -0 are equal; logits are finite), so all keys differ and
+// the slot of a selected expert is its rank: the number of keys above its
+// own.  Each lane ranks its E/64 candidates against all E keys, read back
+// from LDS.  The gates are the softmax of the k selected logits in fp64,
+// summed in slot order, rounded once.  `row` holds the token's E logits
+// (global or shared memory); ids/w receive k entries (and ids_copy, if
+// non-null).  s_key: kTopkKeys keys of LDS scratch for this wave; s_sel: k
+// floats of LDS scratch for this wave.
+constexpr int kTopkKeys = 258;  // E <= 256, plus one pad key for odd E
+__device__ __forceinline__ long long topk_key(float v, int e) {
+  const int b = __float_as_int(v) == (int)0x80000000 ? 0 : __float_as_int(v);
+  const int o = b >= 0 ? b : b ^ 0x7fffffff;  // order-preserving for finite floats
+  return (long long)o * 256 + (255 - e);
+}
+template <int kPer>
+__device__ __forceinline__ void topk_wave_t(const float* row, int E, int k, int32_t* ids, float* w,
+                                            int32_t* ids_copy, long long* s_key, float* s_sel) {
   const int lane = threadIdx.x % kWave;
-  constexpr int kPer = 4;  // E <= 256
-  float v[kPer];
+  long long key[kPer];
+  float val[kPer];
+  int above[kPer];
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const int e = lane + kWave * j;
-    v[j] = e < E ? row[e] : -INFINITY;
+    val[j] = e < E ? row[e] : 0.f;
+    key[j] = e < E ? topk_key(val[j], e) : (long long)INT64_MIN;
+    if (e < E) s_key[e] = key[j];
+    above[j] = 0;
   }
-  unsigned taken = 0;
-  float sel_v = 0.f;
-  int sel_id = 0;
-  for (int s = 0; s < k; ++s) {
-    // best remaining in this lane (lowest id among equals: ids grow with j)
-    float bv = -INFINITY;
-    int bid = 0x7fffffff;
+  if (lane == 0 && (E & 1)) s_key[E] = (long long)INT64_MIN;
+  wave_lds_sync();
+#pragma unroll 4
+  for (int e = 0; e < E; e += 2) {
+    const long long k0 = s_key[e], k1 = s_key[e + 1];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int e = lane + kWave * j;
-      if (e < E && !(taken & (1u << j)) && (v[j] > bv || (v[j] == bv && e < bid))) {
-        bv = v[j];
-        bid = e;
-      }
-    }
+    for (int j = 0; j < kPer; ++j) above[j] += (int)(k0 > key[j]) + (int)(k1 > key[j]);
+  }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oid = __shfl_xor(bid, o, kWave);
-      if (ov > bv || (ov == bv && oid < bid)) {
-        bv = ov;
-        bid = oid;
-      }
-    }
-    if ((bid % kWave) == lane) taken |= 1u << (bid / kWave);
-    if (lane == s) {
-      sel_v = bv;
-      sel_id = bid;
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E && above[j] < k) {
+      ids[above[j]] = e;
+      s_sel[above[j]] = val[j];
+      if (ids_copy) ids_copy[above[j]] = e;
     }
   }
+  wave_lds_sync();
   // Gates: softmax over the selected logits, fp64, slot order, rounded once.
-  const double top = (double)__shfl(sel_v, 0, kWave);
-  const double ex = lane < k ? exp((double)sel_v - top) : 0.0;
+  const double top = (double)s_sel[0];
+  const double ex = lane < k ? exp((double)s_sel[lane] - top) : 0.0;
   double den = 0.0;
-  for (int s = 0; s < k; ++s) den += __shfl(ex, s, kWave);
-  if (lane < k) {
-    ids[lane] = sel_id;
-    w[lane] = (float)(ex / den);
-    if (ids_copy) ids_copy[lane] = sel_id;
-  }
+  for (int s = 0; s < k; ++s) den += readlane_f64(ex, s);
+  if (lane < k) w[lane] = (float)(ex / den);
+}
+__device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* ids, float* w, int32_t* ids_copy,
+                                          long long* s_key, float* s_sel) {
+  if (E <= kWave) topk_wave_t<1>(row, E, k, ids, w, ids_copy, s_key, s_sel);
+  else if (E <= 2 * kWave) topk_wave_t<2>(row, E, k, ids, w, ids_copy, s_key, s_sel);
+  else topk_wave_t<4>(row, E, k, ids, w, ids_copy, s_key, s_sel);
 }
 
 // Row `row` of src by one block of NT threads: s = max|v| / 127 (IEEE
@@ -98,7 +149,7 @@ __device__ __forceinline__ void quant_row_block(const void* __restrict__ src, bo
   };
   float amax = 0.f;
   for (int c = threadIdx.x; c < cols; c += NT) amax = fmaxf(amax, fabsf(load(c)));
-  amax = wave_max(amax);
+  amax = wave_max_dpp(amax);
   if (lane == 0) s_max[wave] = amax;
   __syncthreads();
   amax = s_max[0];
@@ -115,69 +166,79 @@ __device__ __forceinline__ void quant_row_block(const void* __restrict__ src, bo
 }
 
 // Row `row` of src by one wave (the same arithmetic as quant_row_block):
-// 16-byte loads of 8 (bf16) or 4 (fp32) values per lane; for a row of at
-// most 2048 values the row stays in registers between the two passes.
+// 16-byte loads of 8 (bf16) or 4 (fp32) values per lane.  A row of at most
+// 2048 values can be loaded into registers ahead of time (QuantRow::load,
+// issued early so its latency overlaps other work) and quantised later.
 __device__ __forceinline__ float q_to_int(float v, float s) {
   return s != 0.f ? fminf(127.f, fmaxf(-127.f, rintf(__fdiv_rn(v, s)))) : 0.f;
 }
 template <bool kF32>
-__device__ __forceinline__ void quant_row_wave_t(const void* __restrict__ src, int8_t* __restrict__ q,
-                                                 float* __restrict__ scale, int row, int cols) {
-  constexpr int V = kF32 ? 4 : 8;  // values per 16-byte load
-  constexpr int kRegs = 2048 / (kWave * V);  // loads per lane kept in registers
-  const int lane = threadIdx.x % kWave;
-  const uint8_t* base = (const uint8_t*)src + (size_t)row * cols * (kF32 ? 4 : 2);
-  auto val = [&](const u32x4& u, int i) -> float {
-    return kF32 ? __uint_as_float(u[i]) : bf16_bits_to_f32(i % 2 ? (u[i / 2] >> 16) : (u[i / 2] & 0xffffu));
-  };
-  const bool in_regs = cols <= 2048;
+struct QuantRow {
+  static constexpr int V = kF32 ? 4 : 8;             // values per 16-byte load
+  static constexpr int kRegs = 2048 / (kWave * V);   // loads per lane kept in registers
+  static constexpr int kMaxCols = 2048;
   u32x4 keep[kRegs];
-  float amax = 0.f;
-  if (in_regs) {
+
+  __device__ static const uint8_t* base(const void* src, int row, int cols) {
+    return (const uint8_t*)src + (size_t)row * cols * (kF32 ? 4 : 2);
+  }
+  __device__ static float val(const u32x4& u, int i) {
+    return kF32 ? __uint_as_float(u[i]) : bf16_bits_to_f32(i % 2 ? (u[i / 2] >> 16) : (u[i / 2] & 0xffffu));
+  }
+  // cols <= kMaxCols
+  __device__ void load(const void* src, int row, int cols) {
+    const int lane = threadIdx.x % kWave;
+    const uint8_t* b = base(src, row, cols);
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
       const int c = (j * kWave + lane) * V;
-      keep[j] = c < cols ? ld16(base + (size_t)c * (kF32 ? 4 : 2)) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < kRegs; ++j)
-#pragma unroll
-      for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(keep[j], i)));
-  } else {
-    for (int c = lane * V; c < cols; c += kWave * V) {
-      const u32x4 u = ld16(base + (size_t)c * (kF32 ? 4 : 2));
-#pragma unroll
-      for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(u, i)));
+      keep[j] = c < cols ? ld16(b + (size_t)c * (kF32 ? 4 : 2)) : u32x4{0u, 0u, 0u, 0u};
     }
   }
-  amax = wave_max(amax);
-  const float s = __fdiv_rn(amax, 127.0f);
-  if (lane == 0) scale[row] = s;
-  auto put = [&](const u32x4& u, int c) {
+  __device__ static void put(const u32x4& u, float s, int8_t* __restrict__ q, size_t at) {
     uint32_t packed[V / 4];
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       const uint32_t b = (uint32_t)(uint8_t)(int8_t)q_to_int(val(u, i), s);
       if (i % 4 == 0) packed[i / 4] = b; else packed[i / 4] |= b << (8 * (i % 4));
     }
-    if constexpr (V == 8) *reinterpret_cast<u32x2*>(q + (size_t)row * cols + c) = u32x2{packed[0], packed[1]};
-    else *reinterpret_cast<uint32_t*>(q + (size_t)row * cols + c) = packed[0];
-  };
-  if (in_regs) {
-#pragma unroll
-    for (int j = 0; j < kRegs; ++j) {
-      const int c = (j * kWave + lane) * V;
-      if (c < cols) put(keep[j], c);
-    }
-  } else {
-    for (int c = lane * V; c < cols; c += kWave * V) put(ld16(base + (size_t)c * (kF32 ? 4 : 2)), c);
+    if constexpr (V == 8) *reinterpret_cast<u32x2*>(q + at) = u32x2{packed[0], packed[1]};
+    else *reinterpret_cast<uint32_t*>(q + at) = packed[0];
   }
-}
-__device__ __forceinline__ void quant_row_wave(const void* __restrict__ src, bool src_f32, int8_t* __restrict__ q,
-                                               float* __restrict__ scale, int row, int cols) {
-  if (src_f32) quant_row_wave_t<true>(src, q, scale, row, cols);
-  else quant_row_wave_t<false>(src, q, scale, row, cols);
-}
+  // Quantise the row; `loaded`: load() already ran for this row (cols <= kMaxCols).
+  __device__ void quantise(const void* __restrict__ src, int8_t* __restrict__ q, float* __restrict__ scale, int row,
+                           int cols, bool loaded) {
+    const int lane = threadIdx.x % kWave;
+    const uint8_t* b = base(src, row, cols);
+    const bool in_regs = cols <= kMaxCols;
+    if (in_regs && !loaded) load(src, row, cols);
+    float amax = 0.f;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j)
+#pragma unroll
+        for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(keep[j], i)));
+    } else {
+      for (int c = lane * V; c < cols; c += kWave * V) {
+        const u32x4 u = ld16(b + (size_t)c * (kF32 ? 4 : 2));
+#pragma unroll
+        for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(u, i)));
+      }
+    }
+    amax = wave_max_dpp(amax);
+    const float s = __fdiv_rn(amax, 127.0f);
+    if (lane == 0) scale[row] = s;
+    if (in_regs) {
+#pragma unroll
+      for (int j = 0; j < kRegs; ++j) {
+        const int c = (j * kWave + lane) * V;
+        if (c < cols) put(keep[j], s, q, (size_t)row * cols + c);
+      }
+    } else {
+      for (int c = lane * V; c < cols; c += kWave * V) put(ld16(b + (size_t)c * (kF32 ? 4 : 2)), s, q, (size_t)row * cols + c);
+    }
+  }
+};
 
 // The permutation by one block of kPermThreads threads (all in LDS; `lds` is
 // permute_lds_bytes(T, E) bytes of shared memory).  topk_ids may point to

@@ -18,12 +18,20 @@ namespace {
 
 static_assert(kSmallRouteT <= kPermWaves, "one wave per token in the top-k step");
 
+template <bool kF32>
 __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(RoutePermuteArgs a) {
   __shared__ float s_logit[kSmallRouteT * 256];           // T x E logits
   __shared__ int32_t s_ids[kSmallRouteT * 16];            // T x k ids
+  __shared__ long long s_key[kSmallRouteT][kTopkKeys];    // top-k scratch, one row per wave
+  __shared__ float s_sel[kSmallRouteT][16];
   __shared__ uint32_t s_perm[(kSmallRouteT + 31) / 32 * 256 * 3 / 2];  // permute_lds_bytes(T <= 32, E <= 256)
   const int T = a.r.T, E = a.r.E, k = a.r.k;
   const int wave = threadIdx.x / kWave;
+  // int8: the token's row of x is loaded now and quantised after the top-k
+  const bool quant = a.x_q && wave < T;
+  const bool preload = quant && a.r.H <= QuantRow<kF32>::kMaxCols;
+  QuantRow<kF32> xrow;
+  if (preload) xrow.load(a.r.x, wave, a.r.H);
   // 1. logits: partial sums in slice order, rounded once, + bias
   for (int i = threadIdx.x; i < T * E; i += kPermThreads) {
     double s = a.partials[i];
@@ -36,8 +44,9 @@ __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(RoutePermute
   __syncthreads();
   // 2. top-k and gates, one wave per token; int8: the token's quantisation of x
   if (wave < T) {
-    topk_wave(s_logit + wave * E, E, k, a.r.topk_ids + wave * k, a.r.topk_w + wave * k, s_ids + wave * k);
-    if (a.x_q) quant_row_wave(a.r.x, a.r.act_f32, a.x_q, a.x_scale, wave, a.r.H);
+    topk_wave(s_logit + wave * E, E, k, a.r.topk_ids + wave * k, a.r.topk_w + wave * k, s_ids + wave * k,
+              s_key[wave], s_sel[wave]);
+    if (quant) xrow.quantise(a.r.x, a.x_q, a.x_scale, wave, a.r.H, preload);
   }
   __syncthreads();
   // 3. permutation and tile schedule
@@ -53,7 +62,10 @@ hipError_t launch_route_permute_small(const RoutePermuteArgs& a, hipStream_t str
     return hipErrorInvalidValue;
   hipError_t e = launch_route_partials(a.r, a.partials, a.slices, stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(route_finish_kernel, dim3(1), dim3(kPermThreads), 0, stream, a);
+  if (a.r.act_f32)
+    hipLaunchKernelGGL(route_finish_kernel<true>, dim3(1), dim3(kPermThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(route_finish_kernel<false>, dim3(1), dim3(kPermThreads), 0, stream, a);
   return hipGetLastError();
 }
 
