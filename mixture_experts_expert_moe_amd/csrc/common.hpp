@@ -75,6 +75,12 @@ __device__ __forceinline__ u32x4 q4_decode8(uint32_t w, const Q4Block& b) {
   return f;
 }
 
+// Symmetric int8 code of v at scale s (s = max|row| / 127, IEEE division):
+// clamp(rne(v / s), -127, 127); s = 0 gives 0.  Returned as a float.
+__device__ __forceinline__ float quant_i8(float v, float s) {
+  return s != 0.f ? fminf(127.f, fmaxf(-127.f, rintf(__fdiv_rn(v, s)))) : 0.f;
+}
+
 // Plain 16-byte global loads through the vector memory path.
 template <class T>
 __device__ __forceinline__ u32x4 ld16(const T* p) {

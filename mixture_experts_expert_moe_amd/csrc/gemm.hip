@@ -62,6 +62,7 @@ struct Kp {  // kernel parameters
   const void* w_min;
   void* out;
   int K, N, T, R;
+  int tiles_ub;     // upper bound on small tiles (the grid's size), <= the schedule's capacity
 };
 
 // Weight operand of one stage for one 16-row block (A operand).
@@ -337,13 +338,14 @@ template <int WF, bool kGU>
 __global__ __launch_bounds__(kWave* split<kGU>()) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WF>())))
 void grouped_gemm_kernel(Kp p) {
   __shared__ Acc<WF> red[(split<kGU>() > 1 ? split<kGU>() - 1 : 1) * kItemBlocks * 4 * kWave];
-  const int n_tiles = p.sched[0];
   const int per_tile = p.N / item_cols<kGU>();
-  const int total = n_tiles * per_tile;
   const int w = blockIdx.x;
-  if (w >= total) return;
   const int mt = w / per_tile, nt = w % per_tile;
-  const int32_t* tile = p.sched + kSchedHeader + (size_t)mt * kTileInts;
+  // The tile entry is read together with the tile count (one round trip):
+  // the clamped index stays inside the schedule, and an entry past the count
+  // is never used.
+  const i32x4 tile = *reinterpret_cast<const i32x4*>(p.sched + kSchedHeader + (size_t)min(mt, p.tiles_ub - 1) * kTileInts);
+  if (mt >= p.sched[0]) return;
   const int group = tile[0], row0 = tile[1], rows = tile[2];
   const int n0 = nt * item_cols<kGU>();
   switch ((rows + 15) / 16) {
@@ -354,14 +356,22 @@ void grouped_gemm_kernel(Kp p) {
   }
 }
 
+Kp kernel_params(const GemmArgs& a, int64_t tiles) {
+  return Kp{a.act, a.act_q, a.act_scale, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R, (int)tiles};
+}
+
+// Upper bound on small tiles: every non-empty group adds at most one partial tile.
+int64_t tiles_upper_bound(const GemmArgs& a) {
+  return (a.R + kTileRows - 1) / kTileRows + std::min<int64_t>(a.G, a.R);
+}
+
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
-  Kp p{a.act, a.act_q, a.act_scale, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
-  // Upper bound on tiles: every non-empty group adds at most one partial tile.
-  const int64_t tiles = (a.R + kTileRows - 1) / kTileRows + std::min<int64_t>(a.G, a.R);
+  const int64_t tiles = tiles_upper_bound(a);
   const int64_t items = tiles * (a.N / item_cols<kGU>());
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0 || grid > (int64_t)INT32_MAX) return hipErrorInvalidValue;
+  const Kp p = kernel_params(a, tiles);
   switch (a.wfmt) {
     case kF32: hipLaunchKernelGGL((grouped_gemm_kernel<kF32, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
     case kBF16: hipLaunchKernelGGL((grouped_gemm_kernel<kBF16, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;

@@ -72,22 +72,60 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
-// Top-k of one token by one wave.  Every (logit, id) pair gets a 64-bit key
-// that orders larger logits first and, among equal logits, the lower expert
-// id first (+0 and -0 are equal; logits are finite), so all keys differ and
-// the slot of a selected expert is its rank: the number of keys above its
-// own.  Each lane ranks its E/64 candidates against all E keys, read back
-// from LDS.  The gates are the softmax of the k selected logits in fp64,
-// summed in slot order, rounded once.  `row` holds the token's E logits
-// (global or shared memory); ids/w receive k entries (and ids_copy, if
-// non-null).  s_key: kTopkKeys keys of LDS scratch for this wave; s_sel: k
-// floats of LDS scratch for this wave.
+// Top-k by ranks.  Every (logit, id) pair gets a 64-bit key that orders
+// larger logits first and, among equal logits, the lower expert id first (+0
+// and -0 are equal; logits are finite), so all keys differ and the slot of a
+// selected expert is its rank: the number of keys above its own.  The gates
+// are the softmax of the k selected logits in fp64, summed in slot order,
+// rounded once.  Lane l of a wave owns the candidates e = l + 64 j, j < kPer.
 constexpr int kTopkKeys = 258;  // E <= 256, plus one pad key for odd E
 __device__ __forceinline__ long long topk_key(float v, int e) {
   const int b = __float_as_int(v) == (int)0x80000000 ? 0 : __float_as_int(v);
   const int o = b >= 0 ? b : b ^ 0x7fffffff;  // order-preserving for finite floats
   return (long long)o * 256 + (255 - e);
 }
+constexpr long long kNoKey = (long long)INT64_MIN;
+
+// Adds to above[j] the number of keys in s_key[lo, hi) (lo even; s_key[hi]
+// readable when hi is odd) larger than key[j].
+template <int kPer>
+__device__ __forceinline__ void topk_count(const long long* s_key, int lo, int hi, const long long (&key)[kPer],
+                                           int (&above)[kPer]) {
+#pragma unroll 4
+  for (int e = lo; e < hi; e += 2) {
+    const long long k0 = s_key[e], k1 = s_key[e + 1];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) above[j] += (int)(k0 > key[j]) + (int)(k1 > key[j]);
+  }
+}
+
+// Given every candidate's full rank: ids / w (and ids_copy, if non-null)
+// receive the k selected experts in slot order; s_sel: k floats of LDS
+// scratch for this wave.
+template <int kPer>
+__device__ __forceinline__ void topk_select(const float (&val)[kPer], const int (&above)[kPer], int E, int k,
+                                            int32_t* ids, float* w, int32_t* ids_copy, float* s_sel) {
+  const int lane = threadIdx.x % kWave;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    if (e < E && above[j] < k) {
+      ids[above[j]] = e;
+      s_sel[above[j]] = val[j];
+      if (ids_copy) ids_copy[above[j]] = e;
+    }
+  }
+  wave_lds_sync();
+  const double top = (double)s_sel[0];
+  const double ex = lane < k ? exp((double)s_sel[lane] - top) : 0.0;
+  double den = 0.0;
+  for (int s = 0; s < k; ++s) den += readlane_f64(ex, s);
+  if (lane < k) w[lane] = (float)(ex / den);
+}
+
+// Top-k of one token by one wave: each lane ranks its candidates against all
+// E keys, read back from LDS.  `row` holds the token's E logits (global or
+// shared memory); s_key: kTopkKeys keys of LDS scratch for this wave.
 template <int kPer>
 __device__ __forceinline__ void topk_wave_t(const float* row, int E, int k, int32_t* ids, float* w,
                                             int32_t* ids_copy, long long* s_key, float* s_sel) {
@@ -99,34 +137,14 @@ __device__ __forceinline__ void topk_wave_t(const float* row, int E, int k, int3
   for (int j = 0; j < kPer; ++j) {
     const int e = lane + kWave * j;
     val[j] = e < E ? row[e] : 0.f;
-    key[j] = e < E ? topk_key(val[j], e) : (long long)INT64_MIN;
+    key[j] = e < E ? topk_key(val[j], e) : kNoKey;
     if (e < E) s_key[e] = key[j];
     above[j] = 0;
   }
-  if (lane == 0 && (E & 1)) s_key[E] = (long long)INT64_MIN;
+  if (lane == 0 && (E & 1)) s_key[E] = kNoKey;
   wave_lds_sync();
-#pragma unroll 4
-  for (int e = 0; e < E; e += 2) {
-    const long long k0 = s_key[e], k1 = s_key[e + 1];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) above[j] += (int)(k0 > key[j]) + (int)(k1 > key[j]);
-  }
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + kWave * j;
-    if (e < E && above[j] < k) {
-      ids[above[j]] = e;
-      s_sel[above[j]] = val[j];
-      if (ids_copy) ids_copy[above[j]] = e;
-    }
-  }
-  wave_lds_sync();
-  // Gates: softmax over the selected logits, fp64, slot order, rounded once.
-  const double top = (double)s_sel[0];
-  const double ex = lane < k ? exp((double)s_sel[lane] - top) : 0.0;
-  double den = 0.0;
-  for (int s = 0; s < k; ++s) den += readlane_f64(ex, s);
-  if (lane < k) w[lane] = (float)(ex / den);
+  topk_count<kPer>(s_key, 0, E, key, above);
+  topk_select<kPer>(val, above, E, k, ids, w, ids_copy, s_sel);
 }
 __device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* ids, float* w, int32_t* ids_copy,
                                           long long* s_key, float* s_sel) {
@@ -158,84 +176,79 @@ __device__ __forceinline__ void quant_row_block(const void* __restrict__ src, bo
   const float s = __fdiv_rn(amax, 127.0f);
   if (threadIdx.x == 0) scale[row] = s;
   for (int c = threadIdx.x; c < cols; c += NT) {
-    float r = 0.f;
-    if (s != 0.f) r = fminf(127.f, fmaxf(-127.f, rintf(__fdiv_rn(load(c), s))));
-    q[(size_t)row * cols + c] = (int8_t)r;
+    q[(size_t)row * cols + c] = (int8_t)quant_i8(load(c), s);
   }
   __syncthreads();  // s_max is reused by the next row
 }
 
-// Row `row` of src by one wave (the same arithmetic as quant_row_block):
-// 16-byte loads of 8 (bf16) or 4 (fp32) values per lane.  A row of at most
-// 2048 values can be loaded into registers ahead of time (QuantRow::load,
-// issued early so its latency overlaps other work) and quantised later.
-__device__ __forceinline__ float q_to_int(float v, float s) {
-  return s != 0.f ? fminf(127.f, fmaxf(-127.f, rintf(__fdiv_rn(v, s)))) : 0.f;
-}
+// Columns [c0, c1) of one row by one wave, for a row quantised by several
+// waves: 16-byte loads of 8 (bf16) or 4 (fp32) values per lane, kept in
+// registers (load() can be issued early so its latency overlaps other work;
+// a slice longer than the registers hold is streamed).  absmax() gives the
+// slice's max |v|; quantise() writes its codes at the row's scale, the same
+// clamp(rne(v / s), -127, 127) as quant_row_block.
 template <bool kF32>
-struct QuantRow {
-  static constexpr int V = kF32 ? 4 : 8;             // values per 16-byte load
-  static constexpr int kRegs = 2048 / (kWave * V);   // loads per lane kept in registers
-  static constexpr int kMaxCols = 2048;
+struct QuantSlice {
+  static constexpr int V = kF32 ? 4 : 8;  // values per 16-byte load
+  static constexpr int kRegs = 8;         // loads per lane kept in registers
   u32x4 keep[kRegs];
 
-  __device__ static const uint8_t* base(const void* src, int row, int cols) {
-    return (const uint8_t*)src + (size_t)row * cols * (kF32 ? 4 : 2);
-  }
   __device__ static float val(const u32x4& u, int i) {
     return kF32 ? __uint_as_float(u[i]) : bf16_bits_to_f32(i % 2 ? (u[i / 2] >> 16) : (u[i / 2] & 0xffffu));
   }
-  // cols <= kMaxCols
-  __device__ void load(const void* src, int row, int cols) {
+  __device__ static bool in_regs(int c0, int c1) { return c1 - c0 <= kRegs * kWave * V; }
+  __device__ static u32x4 ld(const void* row, int c) { return ld16((const uint8_t*)row + (size_t)c * (kF32 ? 4 : 2)); }
+
+  __device__ void load(const void* row, int c0, int c1) {
+    if (!in_regs(c0, c1)) return;
     const int lane = threadIdx.x % kWave;
-    const uint8_t* b = base(src, row, cols);
 #pragma unroll
     for (int j = 0; j < kRegs; ++j) {
-      const int c = (j * kWave + lane) * V;
-      keep[j] = c < cols ? ld16(b + (size_t)c * (kF32 ? 4 : 2)) : u32x4{0u, 0u, 0u, 0u};
+      const int c = c0 + (j * kWave + lane) * V;
+      if (c < c1) keep[j] = ld(row, c);
     }
   }
-  __device__ static void put(const u32x4& u, float s, int8_t* __restrict__ q, size_t at) {
-    uint32_t packed[V / 4];
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const uint32_t b = (uint32_t)(uint8_t)(int8_t)q_to_int(val(u, i), s);
-      if (i % 4 == 0) packed[i / 4] = b; else packed[i / 4] |= b << (8 * (i % 4));
-    }
-    if constexpr (V == 8) *reinterpret_cast<u32x2*>(q + at) = u32x2{packed[0], packed[1]};
-    else *reinterpret_cast<uint32_t*>(q + at) = packed[0];
-  }
-  // Quantise the row; `loaded`: load() already ran for this row (cols <= kMaxCols).
-  __device__ void quantise(const void* __restrict__ src, int8_t* __restrict__ q, float* __restrict__ scale, int row,
-                           int cols, bool loaded) {
+  __device__ float absmax(const void* row, int c0, int c1) const {
     const int lane = threadIdx.x % kWave;
-    const uint8_t* b = base(src, row, cols);
-    const bool in_regs = cols <= kMaxCols;
-    if (in_regs && !loaded) load(src, row, cols);
     float amax = 0.f;
-    if (in_regs) {
+    if (in_regs(c0, c1)) {
 #pragma unroll
-      for (int j = 0; j < kRegs; ++j)
+      for (int j = 0; j < kRegs; ++j) {
+        const int c = c0 + (j * kWave + lane) * V;
+        if (c < c1)
 #pragma unroll
-        for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(keep[j], i)));
+          for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(keep[j], i)));
+      }
     } else {
-      for (int c = lane * V; c < cols; c += kWave * V) {
-        const u32x4 u = ld16(b + (size_t)c * (kF32 ? 4 : 2));
+      for (int c = c0 + lane * V; c < c1; c += kWave * V) {
+        const u32x4 u = ld(row, c);
 #pragma unroll
         for (int i = 0; i < V; ++i) amax = fmaxf(amax, fabsf(val(u, i)));
       }
     }
-    amax = wave_max_dpp(amax);
-    const float s = __fdiv_rn(amax, 127.0f);
-    if (lane == 0) scale[row] = s;
-    if (in_regs) {
+    return wave_max_dpp(amax);
+  }
+  __device__ static void put(const u32x4& u, float s, int8_t* __restrict__ q) {
+    uint32_t packed[V / 4];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const uint32_t b = (uint32_t)(uint8_t)(int8_t)quant_i8(val(u, i), s);
+      if (i % 4 == 0) packed[i / 4] = b; else packed[i / 4] |= b << (8 * (i % 4));
+    }
+    if constexpr (V == 8) *reinterpret_cast<u32x2*>(q) = u32x2{packed[0], packed[1]};
+    else *reinterpret_cast<uint32_t*>(q) = packed[0];
+  }
+  // q: the row's codes (column 0)
+  __device__ void quantise(const void* row, int c0, int c1, float s, int8_t* __restrict__ q) const {
+    const int lane = threadIdx.x % kWave;
+    if (in_regs(c0, c1)) {
 #pragma unroll
       for (int j = 0; j < kRegs; ++j) {
-        const int c = (j * kWave + lane) * V;
-        if (c < cols) put(keep[j], s, q, (size_t)row * cols + c);
+        const int c = c0 + (j * kWave + lane) * V;
+        if (c < c1) put(keep[j], s, q + c);
       }
     } else {
-      for (int c = lane * V; c < cols; c += kWave * V) put(ld16(b + (size_t)c * (kF32 ? 4 : 2)), s, q, (size_t)row * cols + c);
+      for (int c = c0 + lane * V; c < c1; c += kWave * V) put(ld(row, c), s, q + c);
     }
   }
 };
@@ -431,6 +444,100 @@ __device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* 
       token_row[(size_t)t * kS + k] = row;
       row_token[row] = t;
     }
+  }
+}
+
+// The permutation of a few tokens (T <= 16, so every group holds <= 16 rows
+// and is one partial tile) by one block of kPermThreads threads, with the
+// same results as permute_block.  Every (token, expert) pair has a distinct
+// key e * 256 + t, and everything is a count over the keys:
+//   row of (t, e)   = number of keys below its own (rows are grouped by
+//                     expert, token-ascending inside a group);
+//   offsets[g]      = number of keys with expert < g (g <= E), then the
+//                     shared group's T rows;
+//   slot of g's tile = groups with more rows + groups of the same height and
+//                     lower index (per-height counts and group bitmaps).
+// topk_ids may point to global or shared memory.
+constexpr int kFewTokens = 16;
+__device__ __forceinline__ void permute_few_block(const int32_t* topk_ids, int32_t* __restrict__ offsets,
+                                                  int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
+                                                  int32_t* __restrict__ sched, int T, int E, int k, int S,
+                                                  int big_start) {
+  constexpr int kMaxPairs = kFewTokens * 16;
+  constexpr int kMaskWords = (kMaxGroups + 31) / 32;
+  __shared__ uint32_t s_pkey[kMaxPairs];
+  __shared__ int32_t s_off[kMaxGroups + 1];
+  __shared__ int32_t s_hist[kFewTokens + 1];                // groups per height (1..16)
+  __shared__ uint32_t s_hmask[kFewTokens + 1][kMaskWords];  // groups of each height
+  const int G = E + S, kS = k + S, pairs = T * k;
+  const int tid = threadIdx.x;
+  // 1. keys; clear the height tables
+  for (int i = tid; i < pairs; i += kPermThreads) {
+    const int e = topk_ids[i];
+    s_pkey[i] = (unsigned)e < (unsigned)E ? (uint32_t)e * 256u + (uint32_t)(i / k) : 0xffffffffu;
+  }
+  for (int i = tid; i < (kFewTokens + 1) * (kMaskWords + 1); i += kPermThreads) {
+    if (i < kFewTokens + 1) s_hist[i] = 0;
+    else (&s_hmask[0][0])[i - (kFewTokens + 1)] = 0u;
+  }
+  __syncthreads();
+  // 2. rows of the pairs (threads [0, pairs)) and group offsets (threads from 512)
+  if (tid < pairs) {
+    const uint32_t key = s_pkey[tid];
+    const int t = tid / k, j = tid % k;
+    int row = -1;
+    if (key != 0xffffffffu) {
+      row = 0;
+      for (int i = 0; i < pairs; ++i) row += s_pkey[i] < key ? 1 : 0;
+      row_token[row] = t;
+    }
+    token_row[(size_t)t * kS + j] = row;
+  } else if (tid >= kPermThreads / 2 && tid - kPermThreads / 2 <= E) {
+    const int g = tid - kPermThreads / 2;
+    int off = 0;
+    for (int i = 0; i < pairs; ++i) off += (s_pkey[i] >> 8) < (uint32_t)g ? 1 : 0;
+    s_off[g] = off;
+    offsets[g] = off;
+    if (S && g == E) {
+      s_off[E + 1] = off + T;
+      offsets[E + 1] = off + T;
+    }
+  }
+  __syncthreads();
+  if (S) {
+    for (int t = tid; t < T; t += kPermThreads) {
+      const int row = s_off[E] + t;
+      token_row[(size_t)t * kS + k] = row;
+      row_token[row] = t;
+    }
+  }
+  // 3. heights
+  int n = 0;
+  if (tid < G) {
+    n = s_off[tid + 1] - s_off[tid];
+    if (n > 0) {
+      atomicAdd(&s_hist[n], 1);
+      atomicOr(&s_hmask[n][tid / 32], 1u << (tid % 32));
+    }
+  }
+  __syncthreads();
+  // 4. tiles: taller groups first, then lower group index
+  if (tid < G && n > 0) {
+    int slot = 0;
+    for (int h = n + 1; h <= kFewTokens; ++h) slot += s_hist[h];
+    for (int w = 0; w < tid / 32; ++w) slot += __popc(s_hmask[n][w]);
+    slot += __popc(s_hmask[n][tid / 32] & ((1u << (tid % 32)) - 1u));
+    int32_t* t4 = sched + kSchedHeader + (size_t)slot * kTileInts;
+    t4[0] = tid;
+    t4[1] = s_off[tid];
+    t4[2] = n;
+    t4[3] = 0;
+  }
+  if (tid < kSchedHeader) {
+    int tiles = 0;
+    for (int h = 1; h <= kFewTokens; ++h) tiles += s_hist[h];
+    sched[tid] = tid == kSchedSmall ? tiles : tid == kSchedGroups ? G : tid == kSchedRows ? s_off[G]
+               : tid == kSchedBigStart ? big_start : 0;
   }
 }
 

@@ -40,6 +40,10 @@ SMALL = [
     ("bf16_e16k4s1_t1", 256, 256, 16, 4, 1, 1, "bf16", 0.0),
     ("i8_e32k8s1_t8", 512, 256, 32, 8, 1, 8, "i8", 0.0),
     ("i8_e32k8s1_t71", 512, 256, 32, 8, 1, 71, "i8", 0.0),
+    # I = 512, T at and around the few-token routing limit (16)
+    ("i8_e32k8s1_t13", 512, 512, 32, 8, 1, 13, "i8", 0.0),
+    ("i8_e32k8s1_t16", 512, 512, 32, 8, 1, 16, "i8", 0.0),
+    ("i8_e32k4s1_t17", 512, 512, 32, 4, 1, 17, "i8", 0.0),
     ("q4_e16k4s1_t100_zipf", 256, 256, 16, 4, 1, 100, "q4", 1.1),
     ("q4_e16k2s1_t9", 512, 256, 16, 2, 1, 9, "q4", 0.0),
     # T >= 1024: groups of >= 128 rows go through the big-tile kernels (full 128-row
@@ -113,6 +117,10 @@ def run_steps(name, d):
     g.down()
     y_ref = oracle.down(h_in, offsets, spec.hidden, spec.wt, d["w_down"], d["w_down_scale"], d["w_down_min"])
     if spec.wt == "i8":
+        hq_ref, hs_ref = oracle.quant_rows_i8(h_ref.astype(np.float32))
+        R = h_ref.shape[0]
+        np.testing.assert_array_equal(gh.buf(g.layer, "h_q", np.int8, (R, spec.inter)), hq_ref, err_msg="h_q")
+        np.testing.assert_array_equal(gh.buf(g.layer, "h_scale", np.float32, (R,)), hs_ref, err_msg="h_scale")
         np.testing.assert_array_equal(g.y_raw(), y_ref.astype(np.float32), err_msg="int8 down (exact)")
     else:
         gh.assert_close(g.y(), y_ref, what="down y", **tol)
