@@ -256,14 +256,19 @@ __device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int 
 
   AStage a0[U][NA], a1[U][NA];
   BStage<WF> b0[U][NSUB], b1[U][NSUB];
-  auto load = [&](AStage (&a)[U][NA], BStage<WF> (&b)[U][NSUB], int kb) {
+  // Weight loads need only the tile; token loads (gate/up) also need the
+  // rows' tokens, so every batch issues its weights first.
+  auto load_w = [&](AStage (&a)[U][NA], int kb) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int n = 0; n < NA; ++n) load_a<WF>(a[u][n], p, wrow[n], kb + u * KS, q);
+  };
+  auto load_t = [&](BStage<WF> (&b)[U][NSUB], int kb) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int s = 0; s < NSUB; ++s) load_b<WF>(b[u][s], p, arow[s], kb + u * KS, q);
-    }
   };
   auto compute = [&](const AStage (&a)[U][NA], const BStage<WF> (&b)[U][NSUB]) {
 #pragma unroll
@@ -279,12 +284,36 @@ __device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int 
   const int ubeg = wave * units / kSplit, uend = (wave + 1) * units / kSplit;
   const int nb = (uend - ubeg) * (KP / KB);
   const int kbase = ubeg * KP;
-  if (nb > 0) load(a0, b0, kbase);
+  // The first two batches.  Gate/up: both batches' weights go out before
+  // the token loads, which wait for the rows' tokens; down (rows index h
+  // directly): batch by batch, so the first batch does not wait for the
+  // second (loads retire in order).
+  if constexpr (kGU) {
+    if (nb > 0) load_w(a0, kbase);
+    if (nb > 1) load_w(a1, kbase + KB);
+    if (nb > 0) load_t(b0, kbase);
+    if (nb > 1) load_t(b1, kbase + KB);
+  } else {
+    if (nb > 0) {
+      load_w(a0, kbase);
+      load_t(b0, kbase);
+    }
+    if (nb > 1) {
+      load_w(a1, kbase + KB);
+      load_t(b1, kbase + KB);
+    }
+  }
   for (int i = 0; i < nb; i += 2) {
-    if (i + 1 < nb) load(a1, b1, kbase + (i + 1) * KB);
     compute(a0, b0);
-    if (i + 2 < nb) load(a0, b0, kbase + (i + 2) * KB);
+    if (i + 2 < nb) {
+      load_w(a0, kbase + (i + 2) * KB);
+      load_t(b0, kbase + (i + 2) * KB);
+    }
     if (i + 1 < nb) compute(a1, b1);
+    if (i + 3 < nb) {
+      load_w(a1, kbase + (i + 3) * KB);
+      load_t(b1, kbase + (i + 3) * KB);
+    }
   }
   // Cross-wave reduction: waves 1..3 park their partials, wave 0 adds them in order.
   if (wave > 0) {
@@ -330,29 +359,45 @@ constexpr int item_cols() { return kGU ? 32 : 64; }
 #define MOE_GEMM_WAVES_PER_SIMD 2
 #endif
 // Occupancy target: two waves per SIMD keeps enough loads in flight; the
-// 4-bit path needs more registers for its dequantised operands.
-template <int WF>
-constexpr int waves_per_simd() { return WF == kQ4 ? 1 : MOE_GEMM_WAVES_PER_SIMD; }
+// 4-bit path needs more registers for its dequantised operands, unless an
+// item holds at most 32 rows (kSub = 2).
+template <int WF, int kSub>
+constexpr int waves_per_simd() { return WF == kQ4 && kSub > 2 ? 1 : MOE_GEMM_WAVES_PER_SIMD; }
 
-template <int WF, bool kGU>
-__global__ __launch_bounds__(kWave* split<kGU>()) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WF>())))
+// Items cover at most kSub 16-row blocks of a tile: a 64-row tile is cut
+// into 64 / (16 kSub) row chunks, each its own item (an empty chunk exits).
+// kSub = 4: one item per tile.  The 4-bit down GEMM of calls with enough
+// tokens uses kSub = 2: half the registers, so twice the waves per SIMD and
+// twice the loads in flight, for a second read of a tall tile's weights
+// (the shared expert's); a few-token call (tiles of one block) keeps kSub = 4,
+// where the extra, empty chunks only cost dispatch time.
+template <int WF, bool kGU, int kSub>
+__global__ __launch_bounds__(kWave* split<kGU>()) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WF, kSub>())))
 void grouped_gemm_kernel(Kp p) {
-  __shared__ Acc<WF> red[(split<kGU>() > 1 ? split<kGU>() - 1 : 1) * kItemBlocks * 4 * kWave];
+  __shared__ Acc<WF> red[(split<kGU>() > 1 ? split<kGU>() - 1 : 1) * kItemBlocks * kSub * kWave];
+  constexpr int kChunks = 4 / kSub, kChunkRows = 16 * kSub;
+  static_assert(kChunks * kChunkRows == kTileRows, "chunks cover a tile");
   const int per_tile = p.N / item_cols<kGU>();
   const int w = blockIdx.x;
-  const int mt = w / per_tile, nt = w % per_tile;
+  const int mt = w / (per_tile * kChunks), rem = w % (per_tile * kChunks);
+  const int chunk = rem / per_tile, nt = rem % per_tile;
   // The tile entry is read together with the tile count (one round trip):
   // the clamped index stays inside the schedule, and an entry past the count
   // is never used.
   const i32x4 tile = *reinterpret_cast<const i32x4*>(p.sched + kSchedHeader + (size_t)min(mt, p.tiles_ub - 1) * kTileInts);
-  if (mt >= p.sched[0]) return;
-  const int group = tile[0], row0 = tile[1], rows = tile[2];
+  const int n_tiles = p.sched[0];
+  // both loads complete here, before the exit test (one round trip, not two)
+  asm volatile("" ::"s"(tile[0]), "s"(tile[1]), "s"(tile[2]), "s"(n_tiles));
+  if (mt >= n_tiles) return;
+  const int group = tile[0], row0 = tile[1] + chunk * kChunkRows;
+  const int rows = min(kChunkRows, tile[2] - chunk * kChunkRows);
+  if (rows <= 0) return;
   const int n0 = nt * item_cols<kGU>();
   switch ((rows + 15) / 16) {
     case 1: gemm_item<WF, kGU, 1>(p, group, row0, rows, n0, red); break;
-    case 2: gemm_item<WF, kGU, 2>(p, group, row0, rows, n0, red); break;
-    case 3: gemm_item<WF, kGU, 3>(p, group, row0, rows, n0, red); break;
-    default: gemm_item<WF, kGU, 4>(p, group, row0, rows, n0, red); break;
+    case 2: gemm_item<WF, kGU, kSub >= 2 ? 2 : 1>(p, group, row0, rows, n0, red); break;
+    case 3: gemm_item<WF, kGU, kSub >= 3 ? 3 : 1>(p, group, row0, rows, n0, red); break;
+    default: gemm_item<WF, kGU, kSub >= 4 ? 4 : 1>(p, group, row0, rows, n0, red); break;
   }
 }
 
@@ -365,21 +410,33 @@ int64_t tiles_upper_bound(const GemmArgs& a) {
   return (a.R + kTileRows - 1) / kTileRows + std::min<int64_t>(a.G, a.R);
 }
 
-template <bool kGU>
-hipError_t launch(const GemmArgs& a, hipStream_t stream) {
+template <int WF, bool kGU, int kSub>
+hipError_t launch_fmt(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = tiles_upper_bound(a);
-  const int64_t items = tiles * (a.N / item_cols<kGU>());
+  const int64_t items = tiles * (a.N / item_cols<kGU>()) * (4 / kSub);
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0 || grid > (int64_t)INT32_MAX) return hipErrorInvalidValue;
-  const Kp p = kernel_params(a, tiles);
+  hipLaunchKernelGGL((grouped_gemm_kernel<WF, kGU, kSub>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream,
+                     kernel_params(a, tiles));
+  return hipGetLastError();
+}
+
+// 4-bit down GEMMs of calls with at least this many tokens cut tiles into 32-row items.
+constexpr int kQ4DownChunkMinT = 32;
+
+template <bool kGU>
+hipError_t launch(const GemmArgs& a, hipStream_t stream) {
   switch (a.wfmt) {
-    case kF32: hipLaunchKernelGGL((grouped_gemm_kernel<kF32, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
-    case kBF16: hipLaunchKernelGGL((grouped_gemm_kernel<kBF16, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
-    case kI8: hipLaunchKernelGGL((grouped_gemm_kernel<kI8, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
-    case kQ4: hipLaunchKernelGGL((grouped_gemm_kernel<kQ4, kGU>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream, p); break;
+    case kF32: return launch_fmt<kF32, kGU, 4>(a, stream);
+    case kBF16: return launch_fmt<kBF16, kGU, 4>(a, stream);
+    case kI8: return launch_fmt<kI8, kGU, 4>(a, stream);
+    case kQ4:
+      if constexpr (!kGU) {
+        if (a.T >= kQ4DownChunkMinT) return launch_fmt<kQ4, kGU, 2>(a, stream);
+      }
+      return launch_fmt<kQ4, kGU, 4>(a, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace
