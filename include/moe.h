@@ -114,7 +114,7 @@ typedef struct moe_weights {
 /* Caller-owned device buffers shared by the five calls of a layer.  Sizes in
  * bytes come from moe_buffer_sizes (index = position in this struct). */
 typedef struct moe_buffers {
-  float* logits;            /* [max_tokens][E] fp32 router logits, then scratch of moe_route_permute */
+  float* logits;            /* [max_tokens][E] fp32 router logits, then fp64 scratch of the router */
   int32_t* topk_ids;        /* [max_tokens][k] expert ids, descending logit */
   float* topk_w;            /* [max_tokens][k] gates */
   int32_t* expert_offsets;  /* [G+1] first row of each group; [G] = R */
@@ -143,7 +143,9 @@ moe_status moe_buffer_sizes(const moe_desc* desc, size_t sizes[MOE_NUM_BUFFERS])
  *   x:        [T][H] act_dtype
  *   w_router: [E][H] act_dtype
  *   bias:     [E] fp32, or NULL for none
- * Writes bufs->logits, topk_ids, topk_w. */
+ * Writes bufs->logits (a call whose logits would not fill the GPU splits H in
+ * two and keeps the fp64 partial sums in the scratch after the logits),
+ * topk_ids, topk_w. */
 moe_status moe_route_topk(const moe_desc* desc, int32_t T, const void* x, const void* w_router,
                           const float* bias, const moe_buffers* bufs, hipStream_t stream);
 

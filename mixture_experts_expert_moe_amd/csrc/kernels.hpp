@@ -18,6 +18,7 @@ struct RouteArgs {
   float* topk_w;
   int T, H, E, k;
   bool act_f32;
+  double* partials;  // fp64 scratch for the logits of a call split over slices of H (or null)
 };
 
 struct PermuteArgs {
@@ -88,9 +89,14 @@ struct RoutePermuteArgs {
 };
 hipError_t launch_route_partials(const RouteArgs& a, double* partials, int slices, hipStream_t stream);
 hipError_t launch_route_permute_small(const RoutePermuteArgs& a, hipStream_t stream);
+// A call with more tokens whose 16 x 16 logit blocks would not fill the
+// GPU's CUs splits H in kRouteSplit slices (partials summed by the top-k).
+constexpr int kRouteSplit = 2;
 // Bytes of fp64 partials kept after the logits in the logits buffer (max_tokens tokens).
 inline size_t route_partials_bytes(int64_t max_tokens, int64_t E) {
-  return (size_t)kRouteSlices * (size_t)(max_tokens < kSmallRouteT ? max_tokens : kSmallRouteT) * (size_t)E * 8;
+  const int64_t few = (int64_t)kRouteSlices * (max_tokens < kSmallRouteT ? max_tokens : kSmallRouteT);
+  const int64_t many = (int64_t)kRouteSplit * max_tokens;
+  return (size_t)(few > many ? few : many) * (size_t)E * 8;
 }
 inline size_t route_partials_offset(int64_t max_tokens, int64_t E) { return ((size_t)max_tokens * E * 4 + 15) / 16 * 16; }
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);

@@ -116,6 +116,11 @@ moe_status moe_buffer_sizes(const moe_desc* d, size_t sizes[MOE_NUM_BUFFERS]) {
   return MOE_OK;
 }
 
+// fp64 partial logits, kept after the logits in the logits buffer
+double* route_scratch(const moe_desc* d, const moe_buffers* b) {
+  return (double*)((char*)b->logits + moe::route_partials_offset(d->max_tokens, d->n_routed));
+}
+
 moe_status moe_route_topk(const moe_desc* d, int32_t T, const void* x, const void* w_router, const float* bias,
                           const moe_buffers* b, hipStream_t stream) {
   moe_status s = check_call(d, T, b);
@@ -124,7 +129,7 @@ moe_status moe_route_topk(const moe_desc* d, int32_t T, const void* x, const voi
   if (!ptr_ok(b->logits) || !ptr_ok(b->topk_ids) || !ptr_ok(b->topk_w)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   moe::RouteArgs a{x, w_router, bias, b->logits, b->topk_ids, b->topk_w, T, d->hidden, d->n_routed, d->top_k,
-                   d->act_dtype == MOE_F32};
+                   d->act_dtype == MOE_F32, route_scratch(d, b)};
   return hip_status(moe::launch_route(a, stream));
 }
 
@@ -168,10 +173,10 @@ moe_status moe_route_permute(const moe_desc* d, int32_t T, const void* x, const 
   const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
   moe::RoutePermuteArgs a{};
   a.r = moe::RouteArgs{x, w_router, bias, b->logits, b->topk_ids, b->topk_w, T, d->hidden, d->n_routed, d->top_k,
-                       d->act_dtype == MOE_F32};
+                       d->act_dtype == MOE_F32, route_scratch(d, b)};
   a.p = moe::PermuteArgs{b->topk_ids, b->expert_offsets, b->row_token, b->token_row, b->sched, T, d->n_routed,
                          d->top_k, d->n_shared, false, (int)moe::sched_big_start(r_max, groups(d))};
-  a.partials = (double*)((char*)b->logits + moe::route_partials_offset(d->max_tokens, d->n_routed));
+  a.partials = route_scratch(d, b);
   a.slices = slices;
   a.x_q = i8 ? b->x_q : nullptr;
   a.x_scale = i8 ? b->x_scale : nullptr;

@@ -22,8 +22,9 @@ constexpr int kRouteWaves = 8;  // waves per block; each takes an eighth of H
 // holds token/expert (l % 16) and loads 8 consecutive h (one 16-byte load for
 // bf16, two for fp32) at h = base + 8 * (l / 16); MFMA step s of the 8 uses
 // element s, so A (x) and B (w_router) see the same permutation of K.
-// kPartial (T <= 16): block x takes slice x of H (gridDim.x slices) and
-// writes its fp64 partial sums, partials[slice][t][e], instead of logits.
+// kPartial: block (x, y, z) takes slice x of H (gridDim.x slices) for tokens
+// 16 z .. 16 z + 15 and writes its fp64 partial sums, partials[slice][t][e],
+// instead of logits.
 template <bool kF32, bool kPartial>
 __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const void* __restrict__ x,
                                                                         const void* __restrict__ wr,
@@ -33,7 +34,7 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
                                                                         int E) {
   __shared__ double part[kRouteWaves][16][17];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int t0 = kPartial ? 0 : blockIdx.x * 16, e0 = blockIdx.y * 16;
+  const int t0 = (kPartial ? blockIdx.z : blockIdx.x) * 16, e0 = blockIdx.y * 16;
   const int r = lane % 16, q = lane / 16;
   const int t = min(t0 + r, T - 1), e = min(e0 + r, E - 1);
   const int hs = kPartial ? H / gridDim.x : H;  // this block's share of H
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
 #pragma unroll
         for (int w = 1; w < kRouteWaves; ++w) s += part[w][tt][ee];
         if constexpr (kPartial) {
-          partials[((size_t)blockIdx.x * T + tt) * E + e0 + ee] = s;
+          partials[((size_t)blockIdx.x * T + t0 + tt) * E + e0 + ee] = s;
         } else {
           float v = (float)s;
           if (bias) v = __fadd_rn(v, bias[e0 + ee]);
@@ -112,25 +113,60 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
   }
 }
 
-// One wave per token: k rounds of a wave arg-max (larger logit first, equal
-// logits -> lower expert id), then the softmax of the k selected logits in fp64.
-// One wave per token.
-__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits,
+// One wave per token: the rank-count top-k and gates of route_permute.hpp.
+// kSlices > 0: the token's logits are first summed from kSlices fp64
+// partials in slice order, rounded once (+ bias), and written out.
+template <int kSlices>
+__global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits_in,
+                                                        const double* __restrict__ partials,
+                                                        const float* __restrict__ bias,
+                                                        float* __restrict__ logits_out,
                                                         int32_t* __restrict__ topk_ids,
                                                         float* __restrict__ topk_w, int T, int E, int k) {
   __shared__ long long s_key[4][kTopkKeys];
   __shared__ float s_sel[4][16];
-  const int wave = threadIdx.x / kWave;
+  __shared__ float s_row[kSlices > 0 ? 4 : 1][256];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  topk_wave(logits + (size_t)t * E, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, nullptr, s_key[wave],
-            s_sel[wave]);
+  const float* row = logits_in + (size_t)t * E;
+  if constexpr (kSlices > 0) {
+    for (int e = lane; e < E; e += kWave) {
+      double s = partials[(size_t)t * E + e];
+#pragma unroll
+      for (int sl = 1; sl < kSlices; ++sl) s += partials[((size_t)sl * T + t) * E + e];
+      float v = (float)s;
+      if (bias) v = __fadd_rn(v, bias[e]);
+      logits_out[(size_t)t * E + e] = v;
+      s_row[wave][e] = v;
+    }
+    wave_lds_sync();
+    row = s_row[wave];
+  }
+  topk_wave(row, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, nullptr, s_key[wave], s_sel[wave]);
 }
 
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
-  dim3 grid((a.T + 15) / 16, (a.E + 15) / 16);
+  const int tb = (a.T + 15) / 16, eb = (a.E + 15) / 16;
+  // too few 16 x 16 blocks to fill the CUs: split H, sum the partials in the top-k
+  const bool split = a.partials && a.T > kSmallRouteT && tb * eb < 256 && a.H % (256 * kRouteSplit) == 0;
+  if (split) {
+    dim3 grid(kRouteSplit, eb, tb);
+    if (a.act_f32)
+      hipLaunchKernelGGL((route_logits_kernel<true, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+                         a.w_router, nullptr, nullptr, a.partials, a.T, a.H, a.E);
+    else
+      hipLaunchKernelGGL((route_logits_kernel<false, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+                         a.w_router, nullptr, nullptr, a.partials, a.T, a.H, a.E);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_topk_kernel<kRouteSplit>, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits,
+                       a.partials, a.bias, a.logits, a.topk_ids, a.topk_w, a.T, a.E, a.k);
+    return hipGetLastError();
+  }
+  dim3 grid(tb, eb);
   if (a.act_f32)
     hipLaunchKernelGGL((route_logits_kernel<true, false>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
                        a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
@@ -139,8 +175,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
                        a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, a.topk_ids, a.topk_w,
-                     a.T, a.E, a.k);
+  hipLaunchKernelGGL(route_topk_kernel<0>, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, nullptr, nullptr,
+                     nullptr, a.topk_ids, a.topk_w, a.T, a.E, a.k);
   return hipGetLastError();
 }
 
