@@ -253,6 +253,38 @@ struct QuantSlice {
   }
 };
 
+// Inclusive prefix sum within aligned segments of kSeg lanes (kSeg a power of
+// two <= 64): row shifts masked at segment starts, then the row broadcasts
+// for 32- and 64-lane segments.  Every lane of the wave must be active.
+template <int kSeg>
+__device__ __forceinline__ int seg_incl_scan(int v) {
+  const int l = (threadIdx.x % kWave) % kSeg;
+  int t;
+  if constexpr (kSeg >= 2) { t = dpp_i32<kDppShr1, 0xf>(0, v); v += l >= 1 ? t : 0; }
+  if constexpr (kSeg >= 4) { t = dpp_i32<kDppShr2, 0xf>(0, v); v += l >= 2 ? t : 0; }
+  if constexpr (kSeg >= 8) { t = dpp_i32<kDppShr4, 0xf>(0, v); v += l >= 4 ? t : 0; }
+  if constexpr (kSeg >= 16) { t = dpp_i32<kDppShr8, 0xf>(0, v); v += l >= 8 ? t : 0; }
+  if constexpr (kSeg >= 32) v += dpp_i32<kDppBcast15, 0xa>(0, v);
+  if constexpr (kSeg >= 64) v += dpp_i32<kDppBcast31, 0xc>(0, v);
+  return v;
+}
+
+// Per-expert exclusive prefix of the popcounts of its W <= kSeg words, and
+// its total: each wave pass takes 64 / kSeg experts, one lane per word.
+template <int kSeg>
+__device__ __forceinline__ void prefix_words(const uint32_t* bits, uint16_t* pre, int32_t* s_cnt, int E, int W) {
+  constexpr int kPer = kWave / kSeg;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  for (int e0 = wave * kPer; e0 < E; e0 += kPermWaves * kPer) {
+    const int e = e0 + lane / kSeg, w = lane % kSeg;
+    const bool in = e < E && w < W;
+    const int c = in ? __popc(bits[e * W + w]) : 0;
+    const int inc = seg_incl_scan<kSeg>(c);
+    if (in) pre[e * W + w] = (uint16_t)(inc - c);
+    if (e < E && w == kSeg - 1) s_cnt[e] = inc;
+  }
+}
+
 // The permutation by one block of kPermThreads threads (all in LDS; `lds` is
 // permute_lds_bytes(T, E) bytes of shared memory).  topk_ids may point to
 // global or shared memory.
@@ -285,6 +317,14 @@ __device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* 
       pre[e] = 0;
       s_cnt[e] = __popc(bits[e]);
     }
+  } else if (W <= kWave) {
+    // 64 / seg experts per wave pass, one lane per word (seg = the power of two >= W)
+    if (W <= 2) prefix_words<2>(bits, pre, s_cnt, E, W);
+    else if (W <= 4) prefix_words<4>(bits, pre, s_cnt, E, W);
+    else if (W <= 8) prefix_words<8>(bits, pre, s_cnt, E, W);
+    else if (W <= 16) prefix_words<16>(bits, pre, s_cnt, E, W);
+    else if (W <= 32) prefix_words<32>(bits, pre, s_cnt, E, W);
+    else prefix_words<64>(bits, pre, s_cnt, E, W);
   } else for (int e = wave; e < E; e += kPermWaves) {
     int base = 0;
     for (int w0 = 0; w0 < W; w0 += kWave) {
