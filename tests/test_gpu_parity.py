@@ -309,3 +309,33 @@ def test_route_permute_matches_separate_calls(case):
         xq, xs = oracle.quantize_x(spec, d["x"])
         np.testing.assert_array_equal(gh.buf(g.layer, "x_q", np.int8, (T, H)), xq)
         np.testing.assert_array_equal(gh.buf(g.layer, "x_scale", np.float32, (T,)), xs)
+
+
+# Planted ties: router rows 5 and 9 copy row 2, so those three experts get
+# equal logits for every token (the top-k must order them 2, 5, 9 wherever
+# they rank), and token 0 is all zeros (every logit is +0: experts 0 .. k-1,
+# equal gates).  T = 40 takes the two-block split of H (moe_route_topk), T = 12
+# the few-token block (moe_route_permute).
+@pytest.mark.parametrize("T, fused", [(40, False), (12, True)], ids=["split_t40", "fused_t12"])
+def test_route_ties_and_zero_token(T, fused):
+    d = case_inputs(512, 256, 16, 4, 1, T, "bf16", seed=9)
+    wr = d["w_router"].copy()
+    wr[5] = wr[2]
+    wr[9] = wr[2]
+    d["w_router"] = wr
+    x = d["x"].copy()
+    x[0] = 0
+    d["x"] = x
+    say("ties T", T, "fused", fused)
+    g = gh.GpuLayer(d)
+    if fused:
+        g.route_permute()
+    else:
+        g.route()
+    ref = oracle.route(d["x"], d["w_router"], 4, None)
+    check_route(g, d, ref)
+    ids = g.ids()
+    np.testing.assert_array_equal(ids[0], [0, 1, 2, 3])
+    for t in range(T):
+        tied = [e for e in ids[t] if e in (2, 5, 9)]
+        assert tied == sorted(tied), (t, ids[t])
