@@ -7,16 +7,22 @@
 // and walks K in super-stages of 128:
 //  * the token rows (operand B, shared by all four waves) are copied from
 //    global memory straight into LDS with global_load_lds_dwordx4, into a ring
-//    of three stages, in a row-major layout whose 16-byte chunks are
+//    of stages, in a row-major layout whose 16-byte chunks are
 //    XOR-swizzled by row so that fragment reads avoid bank conflicts;
 //  * each wave owns 64 weight rows (operand A) and loads them from global
 //    memory directly into registers in the MFMA fragment layout, into a ring
-//    of three register tiles; 4-bit codes are dequantised in registers right
+//    of register tiles; 4-bit codes are dequantised in registers right
 //    before the MFMAs that use them, so every weight byte is read and decoded
 //    once per block and never passes through LDS;
 //  * the loads of super-stage S + 2 are issued before S is computed, so two
 //    super-stages of loads are in flight behind the MFMAs;
-//  * v_mfma_f32_16x16x32_bf16 accumulates a 64 x 128 tile per wave in AGPRs.
+//  * v_mfma_f32_16x16x32_bf16 accumulates a 64 x 128 tile per wave.
+// That is the bf16 layout (one block, one wave per SIMD, per CU).  With 4-bit
+// weights the ring holds two super-stages (loads one ahead), operand
+// fragments are not prefetched and addresses are 32-bit offsets, so a wave
+// fits in half the register file and two blocks share each CU: while one
+// wave decodes 4-bit codes on the VALU the other's MFMAs run, and one block's
+// prologue and epilogue overlap the other's main loop.
 // For 4-bit weights the K order inside a super-stage is permuted so that each
 // lane's 16-byte load is one whole 32-code block (one scale, one min); the
 // token fragments are read from LDS in the same order, which leaves the dot
@@ -37,7 +43,17 @@ namespace {
 
 constexpr int kBN = 256;                 // weight rows per block (4 waves x 64)
 constexpr int kSK = 128;                 // K per super-stage
-constexpr int kRing = 3;                 // super-stages resident (LDS stages and A register tiles)
+// Super-stages resident (LDS stages and A register tiles).  bf16: a ring of
+// three, one block (one wave per SIMD) per CU.  4-bit: a ring of two with
+// 32-bit offsets and no operand prefetch, so that a wave fits in half the
+// register file and two blocks share a CU, each covering the other's load
+// latency, prologue and epilogue.
+#ifndef MOE_BIG_RING_Q4
+#define MOE_BIG_RING_Q4 2
+#endif
+template <int WF>
+constexpr int ring() { return WF == kQ4 ? MOE_BIG_RING_Q4 : 3; }
+static_assert(MOE_BIG_RING_Q4 == 2 || MOE_BIG_RING_Q4 == 3, "ring depth");
 constexpr int kThreads = 256;
 // Token rows per block: kBigTileRows for the big-tile list, kTileRows for the
 // small-tile list.  B stage bytes, and DMA instructions per wave per stage
@@ -72,6 +88,17 @@ __device__ __forceinline__ uint32_t gload_u16(const void* p) {
   asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
   return r;
 }
+// Same loads at a 32-bit byte offset from a uniform base (scalar base + vector offset).
+__device__ __forceinline__ u32x4 gload16(const void* base, uint32_t off) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint32_t gload_u16(const void* base, uint32_t off) {
+  uint32_t r;
+  asm volatile("global_load_ushort %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
+  return r;
+}
 
 // Vector-memory loads each thread issues per super-stage (LDS DMA + A).
 template <int WF, int BM>
@@ -91,10 +118,19 @@ struct ATile {
 // eight MFMA groups of the previous super-stage).  4-bit: group g loads the
 // scale (g even) or min (g odd) of fragment g / 2, and the codes of fragment
 // g / 2 on even g; bf16: fragment g / 2, steps 2 (g % 2) and 2 (g % 2) + 1.
-template <int WF>
-__device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const size_t (&arow)[4], int S, int q, int g) {
+template <int WF, class Row>
+__device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row (&arow)[4], int S, int q, int g) {
   const int b = g / 2;
-  if constexpr (WF == kQ4) {
+  if constexpr (WF == kQ4 && sizeof(Row) == 4) {
+    // 32-bit offsets (the launcher checks that the weights fit)
+    const uint32_t blk2 = 2u * (arow[b] * (uint32_t)(p.K / 32) + S * (kSK / 32) + q);
+    if (g % 2 == 0) {
+      a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
+      a.sc[b] = gload_u16(p.w_scale, blk2);
+    } else {
+      a.mn[b] = gload_u16(p.w_min, blk2);
+    }
+  } else if constexpr (WF == kQ4) {
     const size_t blk = arow[b] * (size_t)(p.K / 32) + S * (kSK / 32) + q;
     if (g % 2 == 0) {
       a.v[b][0] = gload16((const uint8_t*)p.w + arow[b] * (size_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
@@ -124,12 +160,16 @@ __device__ __forceinline__ void tie(ATile<WF>& a) {
 // per wave): it writes the 1 KB at (n wave + i) KB of the stage: rows
 // 4 (n wave + i) + lane / 16, chunk slot lane % 16, which holds the row's
 // chunk slot ^ (row % 16).
-template <int BM>
-__device__ __forceinline__ void load_b_part(uint8_t* stage, const uint8_t* const (&src)[b_dma_per_wave<BM>()], int S,
-                                            int wave, int i) {
+template <int BM, class Src>
+__device__ __forceinline__ void load_b_part(uint8_t* stage, const void* act, const Src (&src)[b_dma_per_wave<BM>()],
+                                            int S, int wave, int i) {
   constexpr int n = b_dma_per_wave<BM>();
-  __builtin_amdgcn_global_load_lds((const void*)(src[i] + (size_t)S * (kSK * 2)),
-                                   (lds_void*)(stage + (n * wave + i) * 1024), 16, 0, 0);
+  const uint8_t* g;
+  if constexpr (sizeof(Src) == 4)
+    g = (const uint8_t*)act + (src[i] + (uint32_t)S * (kSK * 2));  // 32-bit byte offset
+  else
+    g = (const uint8_t*)src[i] + (size_t)S * (kSK * 2);
+  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(stage + (n * wave + i) * 1024), 16, 0, 0);
 }
 
 // Barrier between super-stages.  __syncthreads() would also fence the
@@ -171,16 +211,43 @@ template <int WF, int BM, class IssuePart>
 __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[4][BM / 16], int lr,
                                         int q, IssuePart&& issue_part) {
   constexpr int NG = BM / 64, G = 4 * NG, PPG = 8 / G;  // groups per step, groups, load parts per group
+  constexpr bool kLean = ring<WF>() == 2;
   Q4Block qs[4];
   if constexpr (WF == kQ4) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) qs[b] = q4_block(a.sc[b], a.mn[b]);
   }
+
   // token row 16c + lr, chunk slot b_chunk ^ lr (the row's low 4 bits are lr)
   auto bfrag = [&](int kk, int c) {
     return *reinterpret_cast<const u32x4*>(st + (16 * c + lr) * (kSK * 2) + 16 * (b_chunk<WF>(q, kk) ^ lr));
   };
   u32x4 af[4], bf[4];
+  if constexpr (kLean) {
+    // Two waves per SIMD: no operand prefetch (the other wave's MFMAs cover
+    // the LDS latency and the decode), so that the registers go to occupancy:
+    // per group, the token fragments are read and (first group of a step) the
+    // weight fragments decoded right before the 16 MFMAs that use them.
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int kk = g / NG, c0 = 4 * (g % NG);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pp = 0; pp < PPG; ++pp) issue_part(g * PPG + pp);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bf[i] = bfrag(kk, c0 + i);
+      if (g % NG == 0) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, kk);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[b][c0 + i] = mfma_bf16_16x16x32(af[b], bf[i], acc[b][c0 + i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, 0);
 #pragma unroll
@@ -224,29 +291,39 @@ __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(
 template <int WF, bool kGU, int BM>
 __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, int row0, int rows, int n0) {
   constexpr int kBStage = b_stage_bytes<BM>(), NC = BM / 16, NB = b_dma_per_wave<BM>();
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
+  const int t = threadIdx.x, lane = t % kWave;
+  const int wave = __builtin_amdgcn_readfirstlane(t / kWave);  // uniform: keep it in a scalar register
   const int lr = lane % 16, q = lane / 16;
 
+  constexpr int kRing = ring<WF>(), kAhead = kRing - 1;
+  constexpr bool k32 = kRing == 2;  // 32-bit offsets
+  using Row = typename std::conditional<k32, uint32_t, size_t>::type;
+  using Src = typename std::conditional<k32, uint32_t, const uint8_t*>::type;
   // A rows of this wave's 4 fragments (GU: gate cols i0.., i0+16.., then the up rows).
-  size_t arow[4];
+  Row arow[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     if constexpr (kGU) {
       const int i = n0 + 32 * wave + 16 * (b & 1) + lr;
-      arow[b] = (size_t)group * 2 * p.N + (b < 2 ? i : p.N + i);
+      arow[b] = (Row)group * 2 * p.N + (b < 2 ? i : p.N + i);
     } else {
-      arow[b] = (size_t)group * p.N + n0 + 64 * wave + 16 * b + lr;
+      arow[b] = (Row)group * p.N + n0 + 64 * wave + 16 * b + lr;
     }
   }
   // B sources of this lane's DMA chunks (rows past the tile repeat row 0).
-  const uint8_t* bsrc[NB];
+  Src bsrc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int rr = 4 * (NB * wave + i) + lane / 16;
     const int r = rr < rows ? row0 + rr : row0;
-    const size_t src_row = kGU ? (size_t)min(max(p.row_token[r], 0), p.T - 1) : (size_t)r;
     const int chunk = (lane % 16) ^ (rr % 16);
-    bsrc[i] = (const uint8_t*)p.act + src_row * (size_t)p.K * 2 + 16 * chunk;
+    if constexpr (k32) {
+      const uint32_t src_row = kGU ? (uint32_t)min(max(p.row_token[r], 0), p.T - 1) : (uint32_t)r;
+      bsrc[i] = src_row * (uint32_t)p.K * 2 + 16 * chunk;
+    } else {
+      const size_t src_row = kGU ? (size_t)min(max(p.row_token[r], 0), p.T - 1) : (size_t)r;
+      bsrc[i] = (const uint8_t*)p.act + src_row * (size_t)p.K * 2 + 16 * chunk;
+    }
   }
 
   f32x4 acc[4][NC];
@@ -264,7 +341,7 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   constexpr int L = loads_per_stage<WF, BM>();
   // Part g (0..7) of the loads of super-stage S into slot j.
   auto part = [&](int S, int j, int g) {
-    if (g < NB) load_b_part<BM>(lds + j * kBStage, bsrc, S, wave, g);
+    if (g < NB) load_b_part<BM>(lds + j * kBStage, p.act, bsrc, S, wave, g);
     load_a_part<WF>(p, at[j], arow, S, q, g);
   };
   auto issue = [&](int S, int j) {
@@ -272,15 +349,15 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
     for (int g = 0; g < 8; ++g) part(S, j, g);
   };
   issue(0, 0);
-  issue(min(1, nS - 1), 1);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");  // super-stage 0 landed
+  if constexpr (kAhead > 1) issue(min(1, nS - 1), 1);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * (kAhead - 1)) : "memory");  // super-stage 0 landed
   tie<WF>(at[0]);
   stage_barrier();
   auto step = [&](int S, auto slot) {
     constexpr int j = decltype(slot)::value;
-    const int S2 = min(S + 2, nS - 1);
-    compute<WF, BM>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) { part(S2, (j + 2) % kRing, g); });
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");  // super-stage S + 1 landed
+    const int S2 = min(S + kAhead, nS - 1);
+    compute<WF, BM>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) { part(S2, (j + kAhead) % kRing, g); });
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * (kAhead - 1)) : "memory");  // super-stage S + 1 landed
     tie<WF>(at[(j + 1) % kRing]);
     stage_barrier();
   };
@@ -290,11 +367,12 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   for (; S + kRing <= nS; S += kRing) {
     step(S, std::integral_constant<int, 0>{});
     step(S + 1, std::integral_constant<int, 1>{});
-    step(S + 2, std::integral_constant<int, 2>{});
+    if constexpr (kRing > 2) step(S + 2, std::integral_constant<int, 2 % kRing>{});
   }
   if (S < nS) {
     step(S, std::integral_constant<int, 0>{});
-    if (S + 1 < nS) step(S + 1, std::integral_constant<int, 1>{});
+    if constexpr (kRing > 2)
+      if (S + 1 < nS) step(S + 1, std::integral_constant<int, 1>{});
   }
   // Drain the last (clamped) refills.  Their registers are tied after the wait
   // so that the compiler keeps them reserved until the loads have landed.
@@ -336,9 +414,9 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
 // the CUs that the last big items leave idle, and the column blocks of one
 // row tile (which read the same token rows) share an L2.
 template <int WF, bool kGU, bool kSmall>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ring<WF>() == 2 ? 2 : 1)))
 void big_gemm_kernel(Bp p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[kRing * b_stage_bytes<kBigTileRows>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring<WF>() * b_stage_bytes<kBigTileRows>()];
   const int cols = kGU ? kBN / 2 : kBN;  // output columns per item
   const int per_tile = p.N / cols;
   const int big_items = p.sched[kSchedBig] * per_tile;
@@ -358,9 +436,10 @@ void big_gemm_kernel(Bp p) {
   }
 }
 
-// One wave per SIMD: the accumulators (64 x 128 per wave) and the A register
-// ring need more than half the register file.  (A spill would also add
-// scratch loads to the vmcnt accounting of the ring.)
+// bf16: one wave per SIMD (the accumulators, 64 x 128 per wave, and the
+// three-deep A register ring need more than half the register file); 4-bit:
+// two (see the top of the file).  A spill would add scratch loads to the
+// vmcnt accounting of the ring: the build's assembly check rejects it.
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (a.wfmt != kBF16 && a.wfmt != kQ4) return hipErrorInvalidValue;

@@ -59,8 +59,18 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 
 // Big tiles (128 rows, register-A / LDS-B kernel) for long prefill
 // chunks with bf16 or 4-bit weights; a host-side rule on T alone.
+// The 4-bit big-tile kernel addresses weights and activations with 32-bit
+// byte offsets; layers too large for that keep the small-tile kernel.
+bool q4_offsets_fit(const moe_desc* d) {
+  const int64_t H = d->hidden, I = d->inter, G = d->n_routed + d->n_shared;
+  const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
+  const int64_t lim = (int64_t)1 << 32;
+  return G * 2 * I * (H / 2) < lim && (int64_t)d->max_tokens * H * 2 < lim && r_max * I * 2 < lim;
+}
+
 bool big_tiles(const moe_desc* d, int32_t T) {
-  return T >= moe::kBigTileMinTokens && (d->w_dtype == MOE_BF16 || d->w_dtype == MOE_Q4B32);
+  if (T < moe::kBigTileMinTokens) return false;
+  return d->w_dtype == MOE_BF16 || (d->w_dtype == MOE_Q4B32 && q4_offsets_fit(d));
 }
 
 // With big tiles on, the small tiles of 4-bit weights go through the
