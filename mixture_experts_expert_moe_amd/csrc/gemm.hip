@@ -10,8 +10,11 @@
 // 2026-10-27 trace comment).  The shared expert is one more group of the same
 // launch, as the fused "gate_up_shared" / "silu_down_shared" kernels there do.
 //
-// Work item = (tile of <= 64 rows of one group) x (32 gate/up pairs, or 64
-// down columns); one workgroup per item, its waves splitting K.
+// Work item = (tile of <= 64 rows of one group) x (32 gate/up pairs -- 16 for
+// decode steps of at most 16 tokens, where the few touched experts would
+// otherwise occupy too few CUs -- or 64 down columns); one workgroup per item,
+// its waves splitting K.  Every output element goes through the same
+// instructions whatever the item shape, so results do not depend on it.
 // Within an item:
 //   MFMA A operand = 16 weight rows (lane l: row l % 16, K-group l / 16),
 //   MFMA B operand = 16 token rows  (lane l: row l % 16, same K-group),
@@ -197,7 +200,10 @@ __device__ __forceinline__ void store_down(const Kp& p, int r, int col, const Ac
   store4(p, WF == kF32 || WF == kI8, r, col, v);
 }
 
-constexpr int kItemBlocks = 4;  // 16-row weight blocks per work item
+// 16-row weight blocks per work item: 4 (gate/up: 32 gate/up pairs; down: 64
+// columns), or 2 for the gate/up GEMM of decode steps (16 pairs, twice the
+// items, so that the few touched experts' weights spread over all CUs).
+constexpr int kItemBlocks = 4;
 
 #ifndef MOE_SPLIT_GU
 #define MOE_SPLIT_GU 4
@@ -217,16 +223,19 @@ constexpr int split() { return kGU ? MOE_SPLIT_GU : MOE_SPLIT_DN; }
 // U stages with the next batch's loads in flight while the current one
 // computes.  Partial sums meet in LDS and are added in wave order
 // ((w0 + w1) + w2) + w3, so the result does not depend on scheduling.
-template <int WF, bool kGU, int NSUB>
+template <int WF, bool kGU, int NSUB, int NA>
 __device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int rows, int n0, Acc<WF>* red) {
   constexpr int KS = FmtTraits<WF>::KS;
   constexpr int U = stages<WF, NSUB>();
   constexpr int KB = KS * U;
-  constexpr int NA = kItemBlocks;
+  static_assert(NA == 4 || (NA == 2 && kGU), "item shapes");
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int lr = lane % 16, q = lane / 16;
   size_t wrow[NA];
-  if constexpr (kGU) {
+  if constexpr (kGU && NA == 2) {
+    wrow[0] = (size_t)group * 2 * p.N + n0 + lr;  // gate rows
+    wrow[1] = wrow[0] + p.N;                      // up rows
+  } else if constexpr (kGU) {
     wrow[0] = (size_t)group * 2 * p.N + n0 + lr;  // gate rows
     wrow[1] = wrow[0] + 16;
     wrow[2] = wrow[0] + p.N;                      // up rows
@@ -336,7 +345,9 @@ __device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int 
   for (int s = 0; s < NSUB; ++s) {
     if (16 * s + lr < rows) {
       const int r = row0 + 16 * s + lr;
-      if constexpr (kGU) {
+      if constexpr (kGU && NA == 2) {
+        store_gu<WF>(p, r, n0 + 4 * q, acc[0][s], acc[1][s], group, tok[s]);
+      } else if constexpr (kGU) {
         store_gu<WF>(p, r, n0 + 4 * q, acc[0][s], acc[2][s], group, tok[s]);
         store_gu<WF>(p, r, n0 + 16 + 4 * q, acc[1][s], acc[3][s], group, tok[s]);
       } else {
@@ -347,9 +358,9 @@ __device__ __forceinline__ void gemm_item(const Kp& p, int group, int row0, int 
   }
 }
 
-// Output columns one work item covers: 32 gate/up pairs, or 64 down columns.
-template <bool kGU>
-constexpr int item_cols() { return kGU ? 32 : 64; }
+// Output columns one work item covers: 8 NA gate/up pairs, or 16 NA down columns.
+template <bool kGU, int NA>
+constexpr int item_cols() { return kGU ? 8 * NA : 16 * NA; }
 
 // One launch over (tile x column block) items; the grid is sized on the host
 // from an upper bound and each workgroup takes one item, in schedule order
@@ -371,13 +382,13 @@ constexpr int waves_per_simd() { return WF == kQ4 && kSub > 2 ? 1 : MOE_GEMM_WAV
 // twice the loads in flight, for a second read of a tall tile's weights
 // (the shared expert's); a few-token call (tiles of one block) keeps kSub = 4,
 // where the extra, empty chunks only cost dispatch time.
-template <int WF, bool kGU, int kSub>
+template <int WF, bool kGU, int kSub, int NA>
 __global__ __launch_bounds__(kWave* split<kGU>()) __attribute__((amdgpu_waves_per_eu(waves_per_simd<WF, kSub>())))
 void grouped_gemm_kernel(Kp p) {
-  __shared__ Acc<WF> red[(split<kGU>() > 1 ? split<kGU>() - 1 : 1) * kItemBlocks * kSub * kWave];
+  __shared__ Acc<WF> red[(split<kGU>() > 1 ? split<kGU>() - 1 : 1) * NA * kSub * kWave];
   constexpr int kChunks = 4 / kSub, kChunkRows = 16 * kSub;
   static_assert(kChunks * kChunkRows == kTileRows, "chunks cover a tile");
-  const int per_tile = p.N / item_cols<kGU>();
+  const int per_tile = p.N / item_cols<kGU, NA>();
   const int w = blockIdx.x;
   const int mt = w / (per_tile * kChunks), rem = w % (per_tile * kChunks);
   const int chunk = rem / per_tile, nt = rem % per_tile;
@@ -392,12 +403,12 @@ void grouped_gemm_kernel(Kp p) {
   const int group = tile[0], row0 = tile[1] + chunk * kChunkRows;
   const int rows = min(kChunkRows, tile[2] - chunk * kChunkRows);
   if (rows <= 0) return;
-  const int n0 = nt * item_cols<kGU>();
+  const int n0 = nt * item_cols<kGU, NA>();
   switch ((rows + 15) / 16) {
-    case 1: gemm_item<WF, kGU, 1>(p, group, row0, rows, n0, red); break;
-    case 2: gemm_item<WF, kGU, kSub >= 2 ? 2 : 1>(p, group, row0, rows, n0, red); break;
-    case 3: gemm_item<WF, kGU, kSub >= 3 ? 3 : 1>(p, group, row0, rows, n0, red); break;
-    default: gemm_item<WF, kGU, kSub >= 4 ? 4 : 1>(p, group, row0, rows, n0, red); break;
+    case 1: gemm_item<WF, kGU, 1, NA>(p, group, row0, rows, n0, red); break;
+    case 2: gemm_item<WF, kGU, kSub >= 2 ? 2 : 1, NA>(p, group, row0, rows, n0, red); break;
+    case 3: gemm_item<WF, kGU, kSub >= 3 ? 3 : 1, NA>(p, group, row0, rows, n0, red); break;
+    default: gemm_item<WF, kGU, kSub >= 4 ? 4 : 1, NA>(p, group, row0, rows, n0, red); break;
   }
 }
 
@@ -410,13 +421,13 @@ int64_t tiles_upper_bound(const GemmArgs& a) {
   return (a.R + kTileRows - 1) / kTileRows + std::min<int64_t>(a.G, a.R);
 }
 
-template <int WF, bool kGU, int kSub>
+template <int WF, bool kGU, int kSub, int NA = kItemBlocks>
 hipError_t launch_fmt(const GemmArgs& a, hipStream_t stream) {
   const int64_t tiles = tiles_upper_bound(a);
-  const int64_t items = tiles * (a.N / item_cols<kGU>()) * (4 / kSub);
+  const int64_t items = tiles * (a.N / item_cols<kGU, NA>()) * (4 / kSub);
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   if (grid <= 0 || grid > (int64_t)INT32_MAX) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((grouped_gemm_kernel<WF, kGU, kSub>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream,
+  hipLaunchKernelGGL((grouped_gemm_kernel<WF, kGU, kSub, NA>), dim3(grid), dim3(kWave * split<kGU>()), 0, stream,
                      kernel_params(a, tiles));
   return hipGetLastError();
 }
@@ -424,8 +435,25 @@ hipError_t launch_fmt(const GemmArgs& a, hipStream_t stream) {
 // 4-bit down GEMMs of calls with at least this many tokens cut tiles into 32-row items.
 constexpr int kQ4DownChunkMinT = 32;
 
+#ifndef MOE_GU_HALF_ITEMS_MAX_T
+#define MOE_GU_HALF_ITEMS_MAX_T 16
+#endif
+// Gate/up GEMMs of calls with at most this many tokens use 16-pair items.
+constexpr int kGuHalfItemsMaxT = MOE_GU_HALF_ITEMS_MAX_T;
+
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, hipStream_t stream) {
+  if constexpr (kGU) {
+    if (a.T <= kGuHalfItemsMaxT && a.N % item_cols<true, 2>() == 0) {
+      switch (a.wfmt) {
+        case kF32: return launch_fmt<kF32, true, 4, 2>(a, stream);
+        case kBF16: return launch_fmt<kBF16, true, 4, 2>(a, stream);
+        case kI8: return launch_fmt<kI8, true, 4, 2>(a, stream);
+        case kQ4: return launch_fmt<kQ4, true, 4, 2>(a, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
+  }
   switch (a.wfmt) {
     case kF32: return launch_fmt<kF32, kGU, 4>(a, stream);
     case kBF16: return launch_fmt<kBF16, kGU, 4>(a, stream);
