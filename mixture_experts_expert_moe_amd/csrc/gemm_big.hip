@@ -443,7 +443,8 @@ void big_gemm_kernel(Bp p) {
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (a.wfmt != kBF16 && a.wfmt != kQ4) return hipErrorInvalidValue;
-  if (with_small && a.wfmt != kQ4) return hipErrorInvalidValue;  // bf16 small tiles keep the K-split kernel
+  // bf16 small tiles keep the K-split kernel; 4-bit small tiles always run here
+  if (with_small != (a.wfmt == kQ4)) return hipErrorInvalidValue;
   const int cols = kGU ? kBN / 2 : kBN;
   if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
   Bp p{a.act, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
@@ -456,8 +457,6 @@ hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   if (with_small)
     hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
-  else if (a.wfmt == kQ4)
-    hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
