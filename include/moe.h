@@ -9,6 +9,7 @@
  *   moe_grouped_gemm_gu   one persistent launch: gate/up GEMM of every expert + SwiGLU
  *   moe_grouped_gemm_down one persistent launch: down GEMM of every expert
  *   moe_combine           gate-weighted, atomic-free sum of each token's rows
+ *   moe_combine_rmsnorm   the same, plus the RMSNorm of the result (stacked layers)
  *
  * The layer computed (the pages print no formula; this is the standard reading
  * of "top-8+shared", "GLU" and "concatenated expert GU, N = TOP_K x 2 x IM_EXP"
@@ -205,6 +206,17 @@ moe_status moe_combine(const moe_desc* desc, int32_t T, const float* residual, v
 /* RMSNorm with unit gain for stacked layers: xn[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)),
  * computed in fp32.  x: [T][H] fp32; xn: [T][H] bf16.  H % 256 == 0. */
 moe_status moe_rmsnorm(int32_t T, int32_t H, float eps, const float* x, void* xn, hipStream_t stream);
+
+/* Combine fused with the RMSNorm of its result, for stacked layers
+ * x_{l+1} = x_l + MoE_l(RMSNorm(x_l)): writes out exactly as moe_combine
+ * (fp32 residual stream) and xn = bf16(out[t] / sqrt(mean(out[t]^2) + eps)),
+ * bit for bit what moe_rmsnorm gives on that out, so the next layer's input
+ * needs no launch of its own.
+ *   residual: [T][H] fp32 or NULL;  out: [T][H] fp32;  xn: [T][H] bf16
+ * desc->out_dtype must be MOE_F32 and hidden <= 8192 (else
+ * MOE_ERR_UNSUPPORTED); eps >= 0.  xn may not alias out or residual. */
+moe_status moe_combine_rmsnorm(const moe_desc* desc, int32_t T, const float* residual, float eps, void* out,
+                               void* xn, const moe_buffers* bufs, hipStream_t stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(moe_status s);

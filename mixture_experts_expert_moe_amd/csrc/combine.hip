@@ -1,4 +1,6 @@
-// Gate-weighted combine (moe_combine) and RMSNorm (moe_rmsnorm).
+// Gate-weighted combine (moe_combine), RMSNorm (moe_rmsnorm), and the two
+// fused for stacked layers (moe_combine_rmsnorm: layer l's output and layer
+// l + 1's normalised input in one launch).
 //
 // Combine: each token sums its k routed rows weighted by its gates, then its
 // shared-expert row with weight 1 (the shared expert is always on, "top-8+shared"
@@ -31,15 +33,45 @@ __device__ __forceinline__ void load8(const void* y, size_t off, float v[8]) {
   }
 }
 
-template <bool kYF32, bool kOutF32>
+// RMSNorm reduction shared by the stand-alone kernel and the fused combine:
+// the thread's fp32 sum of squares (its chunks in order, fmaf in element
+// order), an xor-shuffle tree over the wave, the four wave sums as
+// (w0 + w1) + (w2 + w3), then 1 / sqrt(mean + eps) with each operation
+// rounded once.  Both kernels run it in 256-thread blocks, so for the same
+// fp32 row they produce the same bits.
+__device__ __forceinline__ float rms_inv(float ss, int H, float eps, float* s_part) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+  if (lane == 0) s_part[wave] = ss;
+  __syncthreads();
+  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
+  return __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(tot, (float)H), eps)));
+}
+
+__device__ __forceinline__ u32x4 scale_bf16x8(const float v[8], float inv) {
+  return u32x4{pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv),
+               pack_bf16x2(v[4] * inv, v[5] * inv), pack_bf16x2(v[6] * inv, v[7] * inv)};
+}
+
+// Chunks of 8 elements a thread owns in the fused combine + RMSNorm (H <= 8192).
+constexpr int kNormChunks = 4;
+
+// kNorm: the output (fp32) is also normalised into xn (bf16), the input of
+// the next stacked layer, from the values held in registers.
+template <bool kYF32, bool kOutF32, bool kNorm>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y, const int32_t* __restrict__ token_row,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ residual, void* __restrict__ out,
-                                                      int H, int k, int S) {
+                                                      uint16_t* __restrict__ xn, float eps, int H, int k, int S) {
+  static_assert(!kNorm || kOutF32, "the normalised stream is fp32");
+  __shared__ float s_part[4];
   const int t = blockIdx.x;
   const int kS = k + S;
-  for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
-    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  // out[t][c0 .. c0+8) into acc
+  auto chunk = [&](int c0, float (&acc)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     for (int j = 0; j < kS; ++j) {
       const int r = token_row[(size_t)t * kS + j];
       if (r < 0) continue;
@@ -64,6 +96,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
                  pack_bf16x2(acc[6], acc[7])};
       *reinterpret_cast<u32x4*>((uint16_t*)out + (size_t)t * H + c0) = o;
     }
+  };
+  if constexpr (!kNorm) {
+    for (int c0 = threadIdx.x * 8; c0 < H; c0 += 256 * 8) {
+      float acc[8];
+      chunk(c0, acc);
+    }
+  } else {
+    float keep[kNormChunks][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int ch = 0; ch < kNormChunks; ++ch) {
+      const int c0 = threadIdx.x * 8 + ch * 256 * 8;
+      if (c0 < H) {
+        chunk(c0, keep[ch]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss = fmaf(keep[ch][i], keep[ch][i], ss);
+      }
+    }
+    const float inv = rms_inv(ss, H, eps, s_part);
+#pragma unroll
+    for (int ch = 0; ch < kNormChunks; ++ch) {
+      const int c0 = threadIdx.x * 8 + ch * 256 * 8;
+      if (c0 < H) *reinterpret_cast<u32x4*>(xn + (size_t)t * H + c0) = scale_bf16x8(keep[ch], inv);
+    }
   }
 }
 
@@ -72,7 +128,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
                                                       float eps) {
   __shared__ float s_part[4];
   const int t = blockIdx.x;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   float ss = 0.f;
   for (int c0 = threadIdx.x * 8; c0 < H; c0 += 2048) {
     float v[8];
@@ -80,18 +135,11 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 #pragma unroll
     for (int i = 0; i < 8; ++i) ss = fmaf(v[i], v[i], ss);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-  if (lane == 0) s_part[wave] = ss;
-  __syncthreads();
-  const float tot = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
-  const float inv = __fdiv_rn(1.0f, __fsqrt_rn(__fadd_rn(__fdiv_rn(tot, (float)H), eps)));
+  const float inv = rms_inv(ss, H, eps, s_part);
   for (int c0 = threadIdx.x * 8; c0 < H; c0 += 2048) {
     float v[8];
     load8<true>(x, (size_t)t * H + c0, v);
-    u32x4 o = {pack_bf16x2(v[0] * inv, v[1] * inv), pack_bf16x2(v[2] * inv, v[3] * inv),
-               pack_bf16x2(v[4] * inv, v[5] * inv), pack_bf16x2(v[6] * inv, v[7] * inv)};
-    *reinterpret_cast<u32x4*>(xn + (size_t)t * H + c0) = o;
+    *reinterpret_cast<u32x4*>(xn + (size_t)t * H + c0) = scale_bf16x8(v, inv);
   }
 }
 
@@ -99,15 +147,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(a.T), dim3(256), 0, stream, a.y, a.token_row, a.topk_w, a.residual, a.out, a.H,
-                       a.k, a.S);
+    hipLaunchKernelGGL(kern, dim3(a.T), dim3(256), 0, stream, a.y, a.token_row, a.topk_w, a.residual, a.out, a.xn,
+                       a.eps, a.H, a.k, a.S);
   };
-  if (a.y_f32) {
-    if (a.out_f32) go(combine_kernel<true, true>);
-    else go(combine_kernel<true, false>);
+  if (a.xn) {
+    if (!a.out_f32 || a.H > 256 * 8 * kNormChunks) return hipErrorInvalidValue;
+    if (a.y_f32) go(combine_kernel<true, true, true>);
+    else go(combine_kernel<false, true, true>);
+  } else if (a.y_f32) {
+    if (a.out_f32) go(combine_kernel<true, true, false>);
+    else go(combine_kernel<true, false, false>);
   } else {
-    if (a.out_f32) go(combine_kernel<false, true>);
-    else go(combine_kernel<false, false>);
+    if (a.out_f32) go(combine_kernel<false, true, false>);
+    else go(combine_kernel<false, false, false>);
   }
   return hipGetLastError();
 }

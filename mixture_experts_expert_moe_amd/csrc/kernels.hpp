@@ -70,6 +70,8 @@ struct CombineArgs {
   void* out;
   bool out_f32;
   int T, H, k, S;
+  uint16_t* xn = nullptr;  // if set: also xn = bf16 RMSNorm(out) (out fp32, H <= 8192)
+  float eps = 0.f;
 };
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);

@@ -280,6 +280,20 @@ moe_status moe_combine(const moe_desc* d, int32_t T, const float* residual, void
   return hip_status(moe::launch_combine(a, stream));
 }
 
+moe_status moe_combine_rmsnorm(const moe_desc* d, int32_t T, const float* residual, float eps, void* out, void* xn,
+                               const moe_buffers* b, hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  if (!ptr_ok(out) || !ptr_ok(xn) || !ptr_ok(b->y) || !ptr_ok(b->token_row) || !ptr_ok(b->topk_w) ||
+      (residual && !aligned16(residual)) || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (d->out_dtype != MOE_F32 || d->hidden > 8192) return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  moe::CombineArgs a{b->y, f32_intermediates(d), b->token_row, b->topk_w, residual, out, true, T, d->hidden,
+                     d->top_k, d->n_shared, (uint16_t*)xn, eps};
+  return hip_status(moe::launch_combine(a, stream));
+}
+
 moe_status moe_rmsnorm(int32_t T, int32_t H, float eps, const float* x, void* xn, hipStream_t stream) {
   if (T < 0 || H <= 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   if (H % 256) return MOE_ERR_UNSUPPORTED;

@@ -20,7 +20,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 
 # The C-ABI entry points declared in include/moe.h.
 EXPORTS = ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
-           "moe_grouped_gemm_down", "moe_combine", "moe_rmsnorm", "moe_status_string", "moe_abi_version")
+           "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_status_string",
+           "moe_abi_version")
 
 
 class MoeDesc(ctypes.Structure):
@@ -64,12 +65,13 @@ def lib():
         L.moe_grouped_gemm_gu.argtypes = [P(MoeDesc), i32, vp, P(MoeWeights), P(MoeBuffers), vp]
         L.moe_grouped_gemm_down.argtypes = [P(MoeDesc), i32, P(MoeWeights), P(MoeBuffers), vp]
         L.moe_combine.argtypes = [P(MoeDesc), i32, vp, vp, P(MoeBuffers), vp]
+        L.moe_combine_rmsnorm.argtypes = [P(MoeDesc), i32, vp, ctypes.c_float, vp, vp, P(MoeBuffers), vp]
         L.moe_rmsnorm.argtypes = [i32, i32, ctypes.c_float, vp, vp, vp]
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
         for f in ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
-                  "moe_grouped_gemm_down", "moe_combine", "moe_rmsnorm"):
+                  "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -154,6 +156,11 @@ def moe_combine(desc, T, residual, out, bufs: MoeBuffers, stream=None):
                                             _stream(stream)))
 
 
+def moe_combine_rmsnorm(desc, T, residual, eps, out, xn, bufs: MoeBuffers, stream=None):
+    _check("moe_combine_rmsnorm", lib().moe_combine_rmsnorm(ctypes.byref(desc), T, _ptr(residual), eps, _ptr(out),
+                                                            _ptr(xn), ctypes.byref(bufs), _stream(stream)))
+
+
 def moe_rmsnorm(T, H, eps, x, xn, stream=None):
     _check("moe_rmsnorm", lib().moe_rmsnorm(T, H, eps, _ptr(x), _ptr(xn), _stream(stream)))
 
@@ -225,11 +232,25 @@ class MoeStack:
         moe_combine(d, T, x, out, b, stream)
 
     def forward(self, x, stream=None):
-        """All layers on x ([T][H] fp32, T <= max_tokens); returns the tensor holding the result."""
+        """All layers on x ([T][H] fp32, T <= max_tokens); returns the tensor holding the result.
+        The RMSNorm of every layer after the first comes out of the previous
+        layer's combine (moe_combine_rmsnorm): the same bits as layer() gives,
+        one launch fewer per layer."""
         T = x.shape[0]
+        d, bf = self.desc, self.bufs
+        xn = self.xn[:T]
         a, b = x, self.tmp[:T]
-        for l in range(len(self.layers)):
-            self.layer(l, a, b, T, stream)
+        moe_rmsnorm(T, d.hidden, self.eps, a, xn, stream)
+        L = len(self.layers)
+        for l in range(L):
+            w = self.layers[l]
+            moe_route_permute(d, T, xn, w["w_router"], w.get("bias"), bf, stream)
+            moe_grouped_gemm_gu(d, T, xn, self.gu[l], bf, stream)
+            moe_grouped_gemm_down(d, T, self.dn[l], bf, stream)
+            if l + 1 < L:
+                moe_combine_rmsnorm(d, T, a, self.eps, b, xn, bf, stream)
+            else:
+                moe_combine(d, T, a, b, bf, stream)
             a, b = b, a
         if a.data_ptr() != x.data_ptr():
             x.copy_(a)

@@ -111,6 +111,16 @@ def test_calls_reject_before_launch():
     assert status("moe_rmsnorm", -1, 2048, ctypes.c_float(1e-6), FAKE, FAKE, None) == -1
     # bad desc through a compute call
     assert status("moe_combine", by(desc(hidden=100)), 4, None, FAKE, by(b), None) == -2
+    # fused combine + RMSNorm: fp32 output stream only, hidden <= 8192, an xn buffer, eps >= 0
+    f32 = desc(out="f32")
+    eps = ctypes.c_float(1e-6)
+    assert status("moe_combine_rmsnorm", by(d), 4, None, eps, FAKE, FAKE, by(b), None) == -2
+    assert status("moe_combine_rmsnorm", by(desc(out="f32", hidden=8448)), 4, None, eps, FAKE, FAKE, by(b), None) == -2
+    assert status("moe_combine_rmsnorm", by(f32), 4, None, eps, FAKE, None, by(b), None) == -1
+    assert status("moe_combine_rmsnorm", by(f32), 4, None, eps, FAKE, FAKE + 8, by(b), None) == -1
+    assert status("moe_combine_rmsnorm", by(f32), 4, None, ctypes.c_float(-1.0), FAKE, FAKE, by(b), None) == -1
+    assert status("moe_combine_rmsnorm", by(f32), 257, None, eps, FAKE, FAKE, by(b), None) == -3
+    assert status("moe_combine_rmsnorm", by(f32), 4, None, eps, FAKE, FAKE, by(nob), None) == -1
 
 
 def test_zero_tokens_returns_ok_without_launch():
@@ -125,3 +135,5 @@ def test_zero_tokens_returns_ok_without_launch():
     assert status("moe_grouped_gemm_down", by(d), 0, by(w), by(b), None) == 0
     assert status("moe_combine", by(d), 0, None, FAKE, by(b), None) == 0
     assert status("moe_rmsnorm", 0, 2048, ctypes.c_float(1e-6), FAKE, FAKE, None) == 0
+    assert status("moe_combine_rmsnorm", by(desc(out="f32")), 0, None, ctypes.c_float(1e-6), FAKE, FAKE, by(b),
+                  None) == 0
