@@ -14,8 +14,9 @@
 //    of register tiles; 4-bit codes are dequantised in registers right
 //    before the MFMAs that use them, so every weight byte is read and decoded
 //    once per block and never passes through LDS;
-//  * the loads of super-stage S + 2 are issued before S is computed, so two
-//    super-stages of loads are in flight behind the MFMAs;
+//  * the loads of super-stage S + 2 are issued while S is computed, so two
+//    super-stages of loads are in flight behind the MFMAs (bf16; see below
+//    for 4-bit);
 //  * v_mfma_f32_16x16x32_bf16 accumulates a 64 x 128 tile per wave.
 // That is the bf16 layout (one block, one wave per SIMD, per CU).  With 4-bit
 // weights the ring holds two super-stages (loads one ahead), operand
@@ -333,9 +334,11 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
     for (int c = 0; c < NC; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Ring of kRing super-stages.  step(S, j) computes S from slot j while
-  // issuing the loads of S + 2 (clamped to the last super-stage, so that every
-  // step issues the same number of loads and the wait below is a constant)
-  // into slot (j + 2) % 3, which S - 1 used and the barrier closing S - 1 freed.
+  // issuing the loads of S + kAhead (clamped to the last super-stage, so that
+  // every step issues the same number of loads and the wait below is a
+  // constant) into slot (j + kAhead) % kRing, which S - 1 used and the barrier
+  // closing S - 1 freed; it then waits until only the loads issued after
+  // those of S + 1 are outstanding (none with a ring of two).
   ATile<WF> at[kRing];
   const int nS = p.K / kSK;
   constexpr int L = loads_per_stage<WF, BM>();
