@@ -46,11 +46,14 @@ SMALL = [
     ("i8_e32k4s1_t17", 512, 512, 32, 4, 1, 17, "i8", 0.0),
     ("q4_e16k4s1_t100_zipf", 256, 256, 16, 4, 1, 100, "q4", 1.1),
     ("q4_e16k2s1_t9", 512, 256, 16, 2, 1, 9, "q4", 0.0),
+    # the largest expert count and top-k the library takes (256 experts, top-16)
+    ("bf16_e256k16s1_t40", 256, 256, 256, 16, 1, 40, "bf16", 0.0),
     # T >= 1024: groups of >= 128 rows go through the big-tile kernels (full 128-row
     # tiles, a partial big tile when >= 64 rows remain, small tiles for the rest)
     ("bf16_e8k2s1_t1200_big", 256, 256, 8, 2, 1, 1200, "bf16", 0.0),
     ("q4_e8k2s1_t1100_big", 256, 256, 8, 2, 1, 1100, "q4", 0.0),
     ("q4_e16k4s1_t1024_zipf_big", 256, 512, 16, 4, 1, 1024, "q4", 1.1),
+    ("q4_e256k16_t1100_zipf_big", 256, 256, 256, 16, 0, 1100, "q4", 1.1),
 ]
 
 
