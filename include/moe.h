@@ -40,6 +40,8 @@
  *    a negative moe_status and enqueues nothing.  MOE_ERR_HIP reports a launch
  *    error; faults inside a kernel surface at the caller's next synchronisation.
  *  - T == 0 returns MOE_OK and enqueues nothing.
+ *  - The calls of one layer take the same T (the GEMMs size their launches
+ *    from it and read the schedule the permutation wrote for it).
  *  - The same inputs always produce the same bits (no atomics on data, fixed
  *    reduction orders, schedule-independent per-tile arithmetic).
  *  - Pointers must be 16-byte aligned; row-major layouts, last index contiguous.
