@@ -167,21 +167,46 @@ class Runner:
         return wall, U, kms
 
 
-def cpu_baseline(name, T, sample_tokens, batches=3):
-    """The CPU oracle (as it stands) on a bounded sample of the workload: `batches`
-    distinct token batches of `sample_tokens` tokens through one layer."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(name, T, sample_tokens, batches=3, one_thread_tokens=16):
+    """The CPU oracle (as it stands) on a bounded sample of the workload:
+    `batches` distinct token batches of `sample_tokens` tokens through one
+    layer on every core of this process's CPU share, and one batch of
+    `one_thread_tokens` tokens on one thread."""
     from gen import synth
     from oracle import oracle
-    threads = oracle.default_threads()
+    try:
+        share = len(os.sched_getaffinity(0))
+    except AttributeError:
+        share = os.cpu_count() or 1
+    threads = max(1, min(16, share))  # a one-GPU box's CPU share is 16 cores
     inputs = [synth.layer_inputs(name, sample_tokens, stream=424242 + b) for b in range(batches)]
     t0 = time.perf_counter()
     for d in inputs:
         oracle.layer(d, threads=threads)
     dt = time.perf_counter() - t0
+    d1 = synth.layer_inputs(name, one_thread_tokens, stream=434343)
+    t1 = time.perf_counter()
+    oracle.layer(d1, threads=1)
+    dt1 = time.perf_counter() - t1
     return {"value": batches * sample_tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "one_thread_value": one_thread_tokens / dt1,
+            "host_logical_cpus": os.cpu_count(), "affinity_cpus": share, "cpu_model": cpu_model(),
+            "compile_flags": "g++ -O2 -std=c++17 -ffp-contract=off -fno-fast-math -pthread",
             "sample": "%d batches of %d tokens (of the %d-token workload %s), each through one whole layer "
-                      "(routing, permutation, gate/up, down, combine), fp64 C++ oracle, %.1f s wall on %d threads"
-                      % (batches, sample_tokens, T, name, dt, threads)}
+                      "(routing, permutation, gate/up, down, combine), fp64 C++ oracle, %.1f s wall on %d threads; "
+                      "one-thread figure: %d tokens in %.1f s"
+                      % (batches, sample_tokens, T, name, dt, threads, one_thread_tokens, dt1)}
 
 
 def stack_figures():
@@ -259,7 +284,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--rotations", type=int, default=4, help="distinct weight sets cycled per step")
+    ap.add_argument("--rotations", type=int, default=8, help="distinct weight sets cycled per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the int8 T=8 decode figure")
     ap.add_argument("--no-q4", action="store_true", help="skip the 4-bit T=2048 prefill figure")

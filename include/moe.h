@@ -6,8 +6,8 @@
  *   moe_route_topk        router logits, top-k experts and gates per token
  *   moe_permute           group (token, slot) pairs by expert + tile schedule
  *   moe_route_permute     the two above in one call (two launches for a few tokens)
- *   moe_grouped_gemm_gu   one persistent launch: gate/up GEMM of every expert + SwiGLU
- *   moe_grouped_gemm_down one persistent launch: down GEMM of every expert
+ *   moe_grouped_gemm_gu   one launch: gate/up GEMM of every expert + SwiGLU
+ *   moe_grouped_gemm_down one launch: down GEMM of every expert
  *   moe_combine           gate-weighted, atomic-free sum of each token's rows
  *   moe_combine_rmsnorm   the same, plus the RMSNorm of the result (stacked layers)
  *
@@ -107,7 +107,9 @@ typedef struct moe_desc {
  *   F32/BF16: w = [G][N][K] values; scale = min = NULL.
  *   I8:       w = [G][N][K] int8; scale = float [G][N] (w_real = scale * w); min = NULL.
  *   Q4B32:    w = uint8 [G][N][K/2] (byte b of a block: code 2b low nibble, 2b+1 high nibble);
- *             scale, min = fp16 bits [G][N][K/32]; w_real = bf16_rne(scale * q + min). */
+ *             scale, min = fp16 bits [G][N][K/32];
+ *             w_real = bf16_rne(fp32(scale * q + min)): scale * q is exact in fp32, the add
+ *             rounds once to fp32, and that fp32 value is rounded once more to bf16. */
 typedef struct moe_weights {
   const void* w;
   const void* scale;
@@ -178,7 +180,8 @@ moe_status moe_route_permute(const moe_desc* desc, int32_t T, const void* x, con
                              const float* bias, const moe_buffers* bufs, hipStream_t stream);
 
 /* Gate/up projection of every permuted row plus SwiGLU, all groups in one
- * persistent launch over the tile schedule:
+ * launch over the tile schedule (two for bf16 weights and T >= 1024: the
+ * 128-row tiles and the shorter ones):
  *   h[r][i] = silu(x_t . Wg[g][i]) * (x_t . Wu[g][i]),  t = row_token[r], g = group of r.
  * Float weights: MFMA with fp32 accumulation, h stored in the h dtype.
  * I8 weights: exact int32 accumulation of x_q . w, then a = (fp32(acc) * x_scale[t]) * scale[g][n]
@@ -188,7 +191,8 @@ moe_status moe_route_permute(const moe_desc* desc, int32_t T, const void* x, con
 moe_status moe_grouped_gemm_gu(const moe_desc* desc, int32_t T, const void* x, const moe_weights* w_gu,
                                const moe_buffers* bufs, hipStream_t stream);
 
-/* Down projection of every permuted row, all groups in one persistent launch:
+/* Down projection of every permuted row, all groups in one launch (as for
+ * gate/up; I8 weights add the per-row quantisation of h before it):
  *   y[r][n] = h[r] . Wd[g][n].
  * I8 weights: each row of h is first quantised into h_q / h_scale
  * (s = max|h[r]| / 127, q = clamp(rne(h / s), -127, 127)); then

@@ -1,6 +1,9 @@
 // Grouped expert GEMMs: gate/up + SwiGLU (moe_grouped_gemm_gu) and down
-// (moe_grouped_gemm_down), each ONE persistent launch over the device-resident
-// tile schedule, every expert (and the shared expert) included.
+// (moe_grouped_gemm_down), each one launch over the device-resident tile
+// schedule, every expert (and the shared expert) included.  The grid is sized
+// on the host from an upper bound on the work items (one workgroup per item;
+// workgroups past the schedule's item count exit at once), so no host-device
+// round trip is needed to size it.
 //
 // Why one launch: dispatching experts one at a time serialises the layer
 // ("~2.7s fixed per-request TTFT = ~4,900 serialized per-expert NPU execs",
@@ -147,7 +150,10 @@ __device__ __forceinline__ void mma_stage(Acc<WF> (&acc)[NA][NSUB], const AStage
 __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
 
 // SiLU of the int8 path with each fp32 operation rounded once and exp taken
-// in fp64 then rounded, i.e. fp32(exp(-g)) is the correctly rounded value.
+// in fp64 then rounded to fp32.  The device fp64 exp is accurate to about one
+// fp64 ulp, so fp32(exp(-g)) agrees with the host's (also fp64 exp, rounded)
+// except when exp(-g) falls within a few fp64 ulps of an fp32 rounding
+// boundary (probability about 2^-29 per value).
 __device__ __forceinline__ float silu_exact(float g) {
   const float e = (float)exp(-(double)g);
   return __fdiv_rn(g, __fadd_rn(1.0f, e));

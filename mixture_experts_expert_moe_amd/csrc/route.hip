@@ -6,9 +6,12 @@
 // fix"; softmax placement and tie order are readings, see the header).
 //
 // Logits are accumulated in fp64 on the matrix cores (v_mfma_f64_16x16x4f64)
-// and rounded once to fp32, so the fp32 logit is the correctly rounded dot
-// product whatever the summation order.  That makes the top-k decision
-// independent of how the sum is blocked.
+// and rounded once to fp32.  Every bf16 x bf16 (or fp32 x fp32) product is
+// exact in fp64, so fp64 sums in different orders differ only in their last
+// fp64 bits, and they round to the same fp32 logit except when the exact sum
+// lies within those few fp64 ulps of an fp32 rounding boundary (probability
+// about 2^-29 per logit).  Outside those rare cases the top-k decision does
+// not depend on how the sum is blocked.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "route_permute.hpp"

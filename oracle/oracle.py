@@ -223,3 +223,36 @@ def layer(d: dict, threads=None, residual=None, with_steps=False):
         return out, dict(logits=logits, ids=ids, w=w, offsets=offsets, row_token=row_token, token_row=token_row,
                          xq=xq, xs=xs, h=h, y=y)
     return out
+
+
+def stack_layer(d: dict, x: np.ndarray, eps: float, threads=None, with_steps=False):
+    """One layer of the stacked workload on the fp32 residual stream x [T][H]:
+
+        xn     = bf16_rne(x / sqrt(mean(x^2) + eps))       (RMSNorm, unit gain)
+        x_next = fp32(x + MoE(xn))                          (residual added in the combine)
+
+    d holds the layer's weights (gen.synth.layer_weights); its "x" is ignored.
+    The normalised input is rounded once from fp64 to bf16 (the layer's
+    activation format); the MoE output and the residual are summed in fp64
+    inside the combine and rounded once to fp32, the residual stream's format.
+    Returns x_next (float32), and with with_steps also a dict with the bf16
+    input bits, the fp64 MoE output (without residual) and the layer's steps.
+    """
+    x = np.ascontiguousarray(x, np.float32)
+    xn = round_bf16(rmsnorm(x, eps)).astype(np.float32)
+    xn_bits = (xn.view(np.uint32) >> 16).astype(np.uint16)
+    dl = dict(d)
+    dl["x"] = xn_bits
+    out, st = layer(dl, threads=threads, residual=x, with_steps=True)
+    x_next = out.astype(np.float32)
+    if with_steps:
+        moe_out = combine(st["y"], st["token_row"], st["w"])
+        return x_next, dict(st, xn=xn_bits, moe=moe_out)
+    return x_next
+
+
+def stack_forward(layers: list, x: np.ndarray, eps: float, threads=None):
+    """x_{l+1} = x_l + MoE_l(RMSNorm(x_l)) over every layer of `layers` (weight dicts)."""
+    for d in layers:
+        x = stack_layer(d, x, eps, threads=threads)
+    return x

@@ -51,6 +51,9 @@ SMALL = [
     # T >= 1024: groups of >= 128 rows go through the big-tile kernels (full 128-row
     # tiles, a partial big tile when >= 64 rows remain, small tiles for the rest)
     ("bf16_e8k2s1_t1200_big", 256, 256, 8, 2, 1, 1200, "bf16", 0.0),
+    # the expert shape of the pages' model (H 2048, I 512): the bf16 big-tile ring's
+    # main loop runs (16 super-stages of K for gate/up, 4 for down)
+    ("bf16_e8k2s1_t1100_h2048_big", 2048, 512, 8, 2, 1, 1100, "bf16", 0.0),
     ("q4_e8k2s1_t1100_big", 256, 256, 8, 2, 1, 1100, "q4", 0.0),
     ("q4_e16k4s1_t1024_zipf_big", 256, 512, 16, 4, 1, 1024, "q4", 1.1),
     ("q4_e256k16_t1100_zipf_big", 256, 256, 256, 16, 0, 1100, "q4", 1.1),
@@ -193,37 +196,23 @@ def test_layer_int8_decode_full(T):
     say("int8 T=%d: max_rel %.3g rmse %.3g" % (T, mr, rm))
 
 
-def test_layer_q4_zipf_prefill_full_sampled():
-    """T = 2048 with Zipf-skewed routing: routing and permutation compared at
-    full size; outputs of a token sample compared with the oracle run on those
-    tokens alone (each token's output depends on that token only)."""
+def test_layer_q4_zipf_prefill_full():
+    """T = 2048 with Zipf-skewed routing, every token: routing, permutation,
+    every h row, every y row (fed the oracle's h), the combine (fed the
+    oracle's y), then the whole layer end to end."""
     d = synth.layer_inputs("q4_e128_top8_shared_zipf", 2048)
     spec = d["spec"]
-    say("layer q4_e128_top8_shared_zipf T=2048")
-    g = gh.GpuLayer(d)
-    g.route()
-    ref_route = oracle.route(d["x"], d["w_router"], spec.top_k, d["bias"])
-    check_route(g, d, ref_route)
-    g.permute()
-    check_permute(g, oracle.permute(ref_route[1], spec.n_routed, spec.n_shared))
+    say("layer q4_e128_top8_shared_zipf T=2048 (steps)")
+    g = run_steps("q4_e128_top8_shared_zipf", d)
     counts = np.diff(g.offsets())
     assert counts[:spec.n_routed].max() > 64 * 8, "Zipf bias should give one expert many tiles"
-    g.gate_up()
-    g.down()
-    g.combine()
-    gh.torch_mod().cuda.synchronize()
-    rng = np.random.default_rng(7)
-    sample = np.sort(rng.choice(2048, 24, replace=False))
-    sub = dict(d)
-    sub["x"] = np.ascontiguousarray(d["x"][sample])
-    ref, st = oracle.layer(sub, with_steps=True)
-    gh.assert_close(g.output()[sample], ref, what="q4 layer (sampled tokens)", **gh.TOL_BF16)
-    # h rows of the sampled tokens
-    tr = g.token_row()[sample]
-    h = g.h()
-    got = np.stack([h[tr[i]] for i in range(len(sample))])
-    want = np.stack([st["h"][st["token_row"][i]] for i in range(len(sample))])
-    gh.assert_close(got, want, what="q4 h (sampled tokens)", **gh.TOL_BF16)
+    head, small, big = g.sched()
+    assert len(big) > 0 and len(small) > 0
+    say("layer q4_e128_top8_shared_zipf T=2048 (end to end)")
+    g2 = gh.GpuLayer(d)
+    g2.run()
+    mr, rm = gh.assert_close(g2.output(), oracle.layer(d), what="q4 layer (all 2048 tokens)", **gh.TOL_BF16)
+    say("q4 T=2048 full: max_rel %.3g rmse %.3g" % (mr, rm))
 
 
 def test_zero_tokens_is_a_noop():

@@ -38,11 +38,6 @@ def say(*a):
     sys.stdout.flush()
 
 
-def bf16_bits_of(xn64):
-    r = oracle.round_bf16(xn64).astype(np.float32)
-    return (r.view(np.uint32) >> 16).astype(np.uint16)
-
-
 @pytest.fixture(scope="module")
 def stack():
     import torch
@@ -64,19 +59,18 @@ def stack():
 
 
 def oracle_stack(S, xs):
-    """Oracle through all layers for the rows xs ([n][H] fp32); per-layer inputs,
-    bf16 RMSNorm outputs, MoE outputs, logits and ids."""
+    """The oracle's stacked composition (oracle.stack_layer) through all layers
+    for the rows xs ([n][H] fp32): per-layer inputs, bf16 RMSNorm outputs, MoE
+    outputs (without the residual), logits and ids."""
     spec, eps = S["spec"], S["ex"]["eps"]
     x = xs.astype(np.float32)
     recs = []
     for l in range(S["L"]):
-        xn_bits = bf16_bits_of(oracle.rmsnorm(x, eps))
         d = dict(S["host"][l])
-        d["x"] = xn_bits
         d["spec"] = spec
-        y, st = oracle.layer(d, with_steps=True)
-        recs.append(dict(x=x, xn=xn_bits, y=y, logits=st["logits"], ids=st["ids"]))
-        x = (x.astype(np.float64) + y).astype(np.float32)
+        x_next, st = oracle.stack_layer(d, x, eps, with_steps=True)
+        recs.append(dict(x=x, xn=st["xn"], y=st["moe"], logits=st["logits"], ids=st["ids"]))
+        x = x_next
     return x, recs
 
 

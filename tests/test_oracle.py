@@ -401,3 +401,92 @@ def test_rmsnorm_closed_forms():
 def test_round_bf16_ties_to_even():
     v = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -20, -(1 + 2 ** -8), 3.0, 0.0])
     np.testing.assert_array_equal(oracle.round_bf16(v), [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0, 3.0, 0.0])
+
+
+# ---- residual combine and the stacked composition ----------------------------------
+
+def bf16_rne_exact(v):
+    """fp64 -> nearest bf16 value (ties to even) with exact rational arithmetic:
+    the spacing of bf16 numbers in [2^e, 2^(e+1)) is 2^(e-7); v / spacing is
+    rounded to the nearest integer, ties to the even one.  Normal range only."""
+    from fractions import Fraction
+    out = np.empty(np.shape(v))
+    for i, x in enumerate(np.asarray(v, np.float64).reshape(-1)):
+        if x == 0.0:
+            out.flat[i] = 0.0
+            continue
+        f = Fraction(float(x))
+        a = abs(f)
+        e = math.floor(math.log2(a))
+        while Fraction(2) ** e > a:
+            e -= 1
+        while Fraction(2) ** (e + 1) <= a:
+            e += 1
+        sp = Fraction(2) ** (e - 7)
+        q = a / sp
+        n = q.numerator // q.denominator
+        rem = q - n
+        if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+            n += 1
+        r = n * sp
+        out.flat[i] = float(r if f > 0 else -r)
+    return out
+
+
+def test_bf16_rne_exact_helper():
+    v = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -30, -(1 + 2 ** -8), 3.0, 0.0, 255.5, 0.1])
+    np.testing.assert_array_equal(bf16_rne_exact(v)[:7], [1.0, 1 + 2 ** -6, 1 + 2 ** -7, -1.0, 3.0, 0.0, 256.0])
+    assert abs(bf16_rne_exact(v)[7] - 0.1) <= 2 ** -4 * 2 ** -8  # within half a spacing at 0.1
+    np.testing.assert_array_equal(oracle.round_bf16(v), bf16_rne_exact(v))
+
+
+@pytest.mark.parametrize("wt", ["f32", "bf16", "q4"])
+def test_combine_residual_matches_dense(wt):
+    """The combine's residual branch: out = dense layer + residual, element by element."""
+    H, I, E, k, S, T = 128, 64, 16, 4, 1, 9
+    act = "f32" if wt == "f32" else "bf16"
+    d = make_case(H, I, E, k, S, T, wt, act=act, seed=31)
+    res = synth.tokens(d["spec"], 1031, T, stream=5, dtype="f32")
+    out = oracle.layer(d, residual=res)
+    wr = d["w_router"]
+    wr64 = bf16_f64(wr) if wr.dtype == np.uint16 else wr.astype(np.float64)
+    wgu = weights_f64(wt, {"w": d["w_gu"], "scale": d["w_gu_scale"], "min": d["w_gu_min"]})
+    wdn = weights_f64(wt, {"w": d["w_down"], "scale": d["w_down_scale"], "min": d["w_down_min"]})
+    ref = np_dense_layer(x_f64(d), wr64, None, wgu, wdn, E, k, S) + res.astype(np.float64)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
+    # residual alone: zero every expert's down projection
+    d0 = dict(d)
+    d0["w_down"] = np.zeros_like(d["w_down"])
+    if wt == "q4":  # codes 0 with min 0 decode to exactly 0
+        d0["w_down_min"] = np.zeros_like(d["w_down_min"])
+    np.testing.assert_array_equal(oracle.layer(d0, residual=res), res.astype(np.float64))
+
+
+def test_stack_composition_matches_dense():
+    """Three stacked 4-bit layers: x_{l+1} = fp32(x_l + dense_l(bf16(RMSNorm(x_l)))),
+    RMSNorm in numpy fp64, bf16 rounding by exact rational arithmetic, each
+    layer by the dense brute force."""
+    H, I, E, k, S, T, eps = 128, 64, 16, 4, 1, 5, 1e-6
+    spec = LayerSpec(hidden=H, inter=I, n_routed=E, top_k=k, n_shared=S, act="bf16", wt="q4", out="f32")
+    layers = [synth.layer_weights(spec, 1500, l) for l in range(3)]
+    for dl in layers:
+        dl["spec"] = spec
+    x0 = synth.tokens(spec, 1500, T, stream=2, dtype="f32")
+    got = oracle.stack_forward(layers, x0, eps)
+    x = x0.astype(np.float32)
+    for dl in layers:
+        x64 = x.astype(np.float64)
+        xn = bf16_rne_exact(x64 / np.sqrt((x64 ** 2).mean(1, keepdims=True) + eps))
+        wgu = weights_f64("q4", {"w": dl["w_gu"], "scale": dl["w_gu_scale"], "min": dl["w_gu_min"]})
+        wdn = weights_f64("q4", {"w": dl["w_down"], "scale": dl["w_down_scale"], "min": dl["w_down_min"]})
+        y = np_dense_layer(xn, bf16_f64(dl["w_router"]), None, wgu, wdn, E, k, S)
+        x = (x64 + y).astype(np.float32)
+    # fp32 residual stream: the brute force keeps fp64 gates, the oracle fp32 ones
+    np.testing.assert_allclose(got, x, rtol=0, atol=2e-6 * np.abs(x).max())
+    # one layer with steps: the bf16 input and the MoE output without the residual
+    x1, st = oracle.stack_layer(layers[0], x0, eps, with_steps=True)
+    np.testing.assert_array_equal(x1, oracle.stack_forward(layers[:1], x0, eps))
+    x64 = x0.astype(np.float64)
+    xn = bf16_rne_exact(x64 / np.sqrt((x64 ** 2).mean(1, keepdims=True) + eps))
+    np.testing.assert_array_equal(bf16_f64(st["xn"]), xn)
+    np.testing.assert_allclose(st["moe"] + x64, x1.astype(np.float64), rtol=0, atol=2e-6 * np.abs(x1).max())
