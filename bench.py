@@ -89,14 +89,14 @@ def load_traffic(kernel, workload, launch_algo_bytes):
 class Runner:
     """Device-resident inputs of one workload and its MoeLayer."""
 
-    def __init__(self, name, T, rotations, n_batches):
+    def __init__(self, name, T, rotations, n_batches, fused=False):
         import torch
         from gen import synth
         from mixture_experts_expert_moe_amd import moe
         from tests import gpu_harness as gh
 
         self.torch, self.moe = torch, moe
-        self.name, self.T = name, T
+        self.name, self.T, self.fused = name, T, fused
         wid = synth.workload_id(name)
         self.spec = spec = synth.workload(name).spec
         t0 = time.time()
@@ -123,6 +123,13 @@ class Runner:
         w = self.wsets[i % len(self.wsets)]
         gu, dn = self.structs[i % len(self.wsets)]
         x = self.x[i % len(self.x)]
+        if self.fused:  # the whole layer in one launch
+            if ev:
+                ev[0].record()
+            moe.moe_decode_layer(d, T, x, w["w_router"], w.get("bias"), gu, dn, None, 0, 1e-6, self.out, b)
+            if ev:
+                ev[1].record()
+            return
         if ev:
             ev[0].record()
         moe.moe_route_permute(d, T, x, w["w_router"], w.get("bias"), b)
@@ -161,7 +168,7 @@ class Runner:
             for i in range(steps):
                 self.step(warmup + steps + i, evs[i])
             torch.cuda.synchronize()
-            names = ["route_permute", "gate_up", "down", "combine"]
+            names = ["decode_layer"] if self.fused else ["route_permute", "gate_up", "down", "combine"]
             kms = {n: float(np.mean([evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps)]))
                    for j, n in enumerate(names)}
         return wall, U, kms
@@ -268,12 +275,40 @@ def stack_figures():
         g.replay()
     torch.cuda.synchronize()
     t_graph = time.perf_counter() - t
+    # the same decode steps with each layer in one launch (moe_decode_layer)
+    xs = dec.clone()
+    for s in range(4):
+        st.forward_decode(xs[s:s + 1])
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for s in range(dec.shape[0]):
+        st.forward_decode(xs[s:s + 1])
+    torch.cuda.synchronize()
+    t_dec1 = time.perf_counter() - t
+    buf.copy_(dec[0:1])
+    st.forward_decode(buf)
+    torch.cuda.synchronize()
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        st.forward_decode(buf)
+    for s in range(4):
+        g1.replay()
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for s in range(dec.shape[0]):
+        buf.copy_(dec[s:s + 1])
+        g1.replay()
+    torch.cuda.synchronize()
+    t_graph1 = time.perf_counter() - t
     weights = L * spec.groups * (weight_bytes(spec, 2 * spec.inter, spec.hidden) + weight_bytes(spec, spec.hidden,
                                                                                                spec.inter))
     out = {"prefill_tokens_per_s": round(P / t_pre, 1), "prefill_ms": round(t_pre * 1e3, 3),
            "decode_tokens_per_s": round(dec.shape[0] / t_dec, 1),
            "decode_graph_tokens_per_s": round(dec.shape[0] / t_graph, 1),
            "decode_graph_ms_per_token": round(t_graph / dec.shape[0] * 1e3, 4),
+           "decode_one_launch_tokens_per_s": round(dec.shape[0] / t_dec1, 1),
+           "decode_one_launch_graph_tokens_per_s": round(dec.shape[0] / t_graph1, 1),
+           "decode_one_launch_graph_ms_per_token": round(t_graph1 / dec.shape[0] * 1e3, 4),
            "layers": L, "weight_bytes_all_layers": weights}
     del st, dev
     return out
@@ -345,9 +380,9 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_decode:
-        sweep = {}
+        sweep, fsweep = {}, {}
         for Td in (1, 2, 4, 8):
-            rd = Runner("int8_e128_top8_shared", Td, max(args.rotations, 4), args.steps + args.warmup)
+            rd = Runner("int8_e128_top8_shared", Td, args.rotations, args.steps + args.warmup)
             wd, Ud, kd = rd.timed(args.steps, args.warmup)
             msd = wd / args.steps * 1e3
             b = gu_algorithmic_bytes(rd.spec, Td, Ud) + down_algorithmic_bytes(rd.spec, Td, Ud)
@@ -357,12 +392,21 @@ def main():
                 "gemm_hbm_frac": round(b / ((kd["gate_up"] + kd["down"]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
                 "gemm_algorithmic_bytes": b,
             }
+            # the same layer through moe_decode_layer (one launch)
+            rd.fused = True
+            wf, Uf, kf = rd.timed(args.steps, args.warmup)
+            msf = wf / args.steps * 1e3
+            bl = b + 2 * rd.spec.n_routed * rd.spec.hidden  # + the router weights
+            fsweep[Td] = {"tokens_per_s": round(Td / (msf / 1e3), 1), "ms_per_step": round(msf, 5),
+                          "launch_ms": round(kf["decode_layer"], 5), "touched_groups": Uf,
+                          "layer_hbm_frac": round(bl / (kf["decode_layer"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
             del rd
             torch.cuda.empty_cache()
         extra["decode_int8_t8"] = sweep[8]
         extra["decode_int8_sweep"] = {str(t): {k: v for k, v in r.items() if k != "kernel_ms"} for t, r in sweep.items()}
+        extra["decode_int8_one_launch"] = {str(t): r for t, r in fsweep.items()}
     if not args.no_fp32:
-        r1 = Runner("fp32_e16_top2", 16, max(args.rotations, 4), args.steps + args.warmup)
+        r1 = Runner("fp32_e16_top2", 16, args.rotations, args.steps + args.warmup)
         w1, U1, k1 = r1.timed(args.steps, args.warmup)
         ms1 = w1 / args.steps * 1e3
         b1 = gu_algorithmic_bytes(r1.spec, 16, U1) + down_algorithmic_bytes(r1.spec, 16, U1)
@@ -374,7 +418,7 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_q4:
         Tq = 2048
-        rq = Runner("q4_e128_top8_shared_zipf", Tq, max(args.rotations, 4), min(args.steps + args.warmup, 24))
+        rq = Runner("q4_e128_top8_shared_zipf", Tq, args.rotations, min(args.steps + args.warmup, 24))
         stq = max(3, min(args.steps, 12))
         wq, Uq, kq = rq.timed(stq, min(args.warmup, 3))
         msq = wq / stq * 1e3

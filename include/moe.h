@@ -11,6 +11,10 @@
  *   moe_combine           gate-weighted, atomic-free sum of each token's rows
  *   moe_combine_rmsnorm   the same, plus the RMSNorm of the result (stacked layers)
  *
+ * or, for a few tokens (decode steps), one call for all of it:
+ *
+ *   moe_decode_layer      the whole layer in one launch (T <= 16)
+ *
  * The layer computed (the pages print no formula; this is the standard reading
  * of "top-8+shared", "GLU" and "concatenated expert GU, N = TOP_K x 2 x IM_EXP"
  * in "~2.7s fixed per-request TTFT = ~4,900 serialized per-expert NPU execs --
@@ -62,7 +66,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -132,9 +136,13 @@ typedef struct moe_buffers {
   void* y;                  /* [R_max][H] down output per row: F32 for F32/I8 weights, BF16 otherwise */
   int8_t* h_q;              /* [R_max][I] int8 GLU output, requantised per row (I8 only) */
   float* h_scale;           /* [R_max] per-row scale of h_q (I8 only) */
+  uint32_t* sync;           /* 4096 bytes of grid-barrier words for moe_decode_layer: zero them once after
+                               allocation; every completed call leaves them valid for the next one.
+                               Word 640 is the status word: nonzero after a barrier wait timed out (then
+                               the call's results are undefined and the words must be zeroed again). */
 } moe_buffers;
 
-#define MOE_NUM_BUFFERS 13
+#define MOE_NUM_BUFFERS 14
 
 /* Byte size of each moe_buffers member for `desc` (sizes[i] for member i).
  * Host only; touches no device.  Returns MOE_ERR_INVALID_ARG / UNSUPPORTED for
@@ -208,6 +216,33 @@ moe_status moe_grouped_gemm_down(const moe_desc* desc, int32_t T, const moe_weig
  *   out:      [T][H] out_dtype */
 moe_status moe_combine(const moe_desc* desc, int32_t T, const float* residual, void* out,
                        const moe_buffers* bufs, hipStream_t stream);
+
+/* The whole layer for 1 <= T <= 16 tokens in one launch.  Decode steps are
+ * where the cost per dispatched operation, not the arithmetic, sets the time
+ * ("MoE Decode Partition and Submit Floor", section 3; "~2.7s fixed
+ * per-request TTFT = ~4,900 serialized per-expert NPU execs", section
+ * "Evidence").  The launch holds one block per CU and three grid-wide
+ * barriers (it must not share the GPU with work that never finishes;
+ * concurrent calls must not share bufs->sync).
+ *   flags = 0: x is [T][H] bf16 (act_dtype BF16); out = MoE(x) (+ residual if
+ *     not NULL), in out_dtype: the results of moe_route_permute,
+ *     moe_grouped_gemm_gu, moe_grouped_gemm_down and moe_combine(residual).
+ *   flags = MOE_DECODE_NORM_INPUT (one stacked layer): x is the [T][H] fp32
+ *     residual stream; the layer input is xn = bf16(RMSNorm(x, eps)) (the bits
+ *     of moe_rmsnorm) and out = x + MoE(xn) in fp32 (out_dtype must be F32,
+ *     residual must be NULL); out may be x (updated in place).
+ * Either way every buffer the separate calls write (logits, topk_ids,
+ * topk_w, expert_offsets, row_token, token_row, sched, x_q, x_scale, h, h_q,
+ * h_scale, y) holds the same bits as after those calls.
+ *   w_router: [E][H] bf16;  bias: [E] fp32 or NULL
+ *   w_gu, w_down: as for the GEMM calls (BF16, I8 or Q4B32 weights)
+ *   residual: [T][H] fp32 or NULL
+ * Limits (else MOE_ERR_UNSUPPORTED): T * hidden <= 32768, inter <= 512,
+ * hidden <= 8192, weights not F32. */
+#define MOE_DECODE_NORM_INPUT 1
+moe_status moe_decode_layer(const moe_desc* desc, int32_t T, const void* x, const void* w_router, const float* bias,
+                            const moe_weights* w_gu, const moe_weights* w_down, const float* residual,
+                            int32_t flags, float eps, void* out, const moe_buffers* bufs, hipStream_t stream);
 
 /* RMSNorm with unit gain for stacked layers: xn[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)),
  * computed in fp32.  x: [T][H] fp32; xn: [T][H] bf16.  H % 256 == 0. */

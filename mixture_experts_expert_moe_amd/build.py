@@ -16,7 +16,8 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_gfx950.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["route.hip", "route_small.hip", "permute.hip", "gemm.hip", "gemm_big.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "route_small.hip", "permute.hip", "gemm.hip", "gemm_big.hip", "combine.hip", "decode.hip",
+           "moe_api.cpp"]
 # Sources whose kernels issue their own vector loads (inline asm + explicit
 # vmcnt waits): their assembly is checked at build time.
 ASM_CHECKED = ["gemm_big.hip"]

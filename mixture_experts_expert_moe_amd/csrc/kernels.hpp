@@ -112,6 +112,38 @@ hipError_t launch_big_down(const GemmArgs& a, bool with_small, hipStream_t strea
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 hipError_t launch_rmsnorm(const float* x, uint16_t* xn, int T, int H, float eps, hipStream_t stream);
 
+// The whole layer for a few tokens in one launch (decode.hip): (RMSNorm,)
+// routing, permutation, gate/up, down and combine over one block per CU with
+// grid-wide barriers in between.
+constexpr int kDecodeMaxT = 16;
+constexpr int kDecodeSyncBytes = 4096;    // barrier words (zero before the first launch)
+constexpr int kDecodeMaxTH = 32768;       // T * H: the int8 path keeps every token's codes in LDS
+constexpr int kDecodeMaxI = 512;          // staged h rows of four down items in LDS
+struct DecodeArgs {
+  const void* x;            // [T][H] bf16 layer input, or (norm_input) the fp32 residual stream
+  const void* w_router;
+  const float* bias;
+  const void* w_gu; const void* gu_scale; const void* gu_min;
+  const void* w_dn; const void* dn_scale; const void* dn_min;
+  const float* residual;    // [T][H] fp32 or null (not with norm_input: x is the residual)
+  void* out;                // [T][H] out dtype
+  float eps;                // RMSNorm epsilon (norm_input)
+  bool norm_input;          // layer input = bf16(RMSNorm(x)), out = x + MoE(that), fp32
+  // layer buffers (same meaning as for the separate calls)
+  float* logits; int32_t* topk_ids; float* topk_w; int32_t* offsets; int32_t* row_token; int32_t* token_row;
+  int32_t* sched; int8_t* x_q; float* x_scale; void* h; void* y; int8_t* h_q; float* h_scale;
+  double* partials;         // fp64 router partial sums [slices][T][E]
+  uint32_t* sync;           // kDecodeSyncBytes of barrier words
+  int T, H, I, E, k, S, wfmt, big_start;
+  bool out_f32;
+  long long spin_ns;        // bound on one barrier wait (then the status word is set and the wait ends)
+};
+hipError_t launch_decode_layer(const DecodeArgs& a, hipStream_t stream);
+// Blocks of the decode launch on this device (0 if the device cannot host it).
+int decode_blocks();
+// Word of the sync buffer that a timed-out barrier wait sets to nonzero.
+constexpr int kDecodeStatusWord = 64 * 10;
+
 // Dynamic LDS bytes the permutation kernel needs for T tokens and E experts:
 // a 32-bit word of token bits plus a 16-bit prefix per (expert, 32 tokens).
 inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)((T + 31) / 32) * (size_t)E * 6; }

@@ -123,6 +123,7 @@ moe_status moe_buffer_sizes(const moe_desc* d, size_t sizes[MOE_NUM_BUFFERS]) {
   sizes[10] = Rmax * H * fw;                             // y
   sizes[11] = i8 ? Rmax * I : 0;                         // h_q
   sizes[12] = i8 ? Rmax * 4 : 0;                         // h_scale
+  sizes[13] = moe::kDecodeSyncBytes;                     // sync
   return MOE_OK;
 }
 
@@ -292,6 +293,74 @@ moe_status moe_combine_rmsnorm(const moe_desc* d, int32_t T, const float* residu
   moe::CombineArgs a{b->y, f32_intermediates(d), b->token_row, b->topk_w, residual, out, true, T, d->hidden,
                      d->top_k, d->n_shared, (uint16_t*)xn, eps};
   return hip_status(moe::launch_combine(a, stream));
+}
+
+moe_status moe_decode_layer(const moe_desc* d, int32_t T, const void* x, const void* w_router, const float* bias,
+                            const moe_weights* w_gu, const moe_weights* w_down, const float* residual,
+                            int32_t flags, float eps, void* out, const moe_buffers* b, hipStream_t stream) {
+  moe_status s = check_call(d, T, b);
+  if (s != MOE_OK) return s;
+  if ((s = check_weights(d, w_gu)) != MOE_OK || (s = check_weights(d, w_down)) != MOE_OK) return s;
+  const bool i8 = d->w_dtype == MOE_I8;
+  const bool norm = (flags & MOE_DECODE_NORM_INPUT) != 0;
+  if ((flags & ~MOE_DECODE_NORM_INPUT) != 0 || (norm && residual)) return MOE_ERR_INVALID_ARG;
+  if (!ptr_ok(x) || !ptr_ok(w_router) || (bias && !aligned16(bias)) || !ptr_ok(out) ||
+      (residual && !aligned16(residual)) || !(eps >= 0.0f))
+    return MOE_ERR_INVALID_ARG;
+  if (!ptr_ok(b->logits) || !ptr_ok(b->topk_ids) || !ptr_ok(b->topk_w) || !ptr_ok(b->expert_offsets) ||
+      !ptr_ok(b->row_token) || !ptr_ok(b->token_row) || !ptr_ok(b->sched) || !ptr_ok(b->h) || !ptr_ok(b->y) ||
+      !ptr_ok(b->sync))
+    return MOE_ERR_INVALID_ARG;
+  if (i8 && (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale) || !ptr_ok(b->h_q) || !ptr_ok(b->h_scale)))
+    return MOE_ERR_INVALID_ARG;
+  if (d->act_dtype != MOE_BF16 || d->w_dtype == MOE_F32 || (norm && d->out_dtype != MOE_F32))
+    return MOE_ERR_UNSUPPORTED;
+  if (T > moe::kDecodeMaxT || (int64_t)T * d->hidden > moe::kDecodeMaxTH || d->inter > moe::kDecodeMaxI ||
+      d->hidden > 8192)
+    return MOE_ERR_UNSUPPORTED;
+  if (T == 0) return MOE_OK;
+  if (moe::decode_blocks() == 0) return MOE_ERR_UNSUPPORTED;
+  const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
+  moe::DecodeArgs a{};
+  a.x = x;
+  a.w_router = w_router;
+  a.bias = bias;
+  a.w_gu = w_gu->w;
+  a.gu_scale = w_gu->scale;
+  a.gu_min = w_gu->min;
+  a.w_dn = w_down->w;
+  a.dn_scale = w_down->scale;
+  a.dn_min = w_down->min;
+  a.residual = residual;
+  a.out = out;
+  a.eps = eps;
+  a.norm_input = norm;
+  a.logits = b->logits;
+  a.topk_ids = b->topk_ids;
+  a.topk_w = b->topk_w;
+  a.offsets = b->expert_offsets;
+  a.row_token = b->row_token;
+  a.token_row = b->token_row;
+  a.sched = b->sched;
+  a.x_q = b->x_q;
+  a.x_scale = b->x_scale;
+  a.h = b->h;
+  a.y = b->y;
+  a.h_q = b->h_q;
+  a.h_scale = b->h_scale;
+  a.partials = route_scratch(d, b);
+  a.sync = b->sync;
+  a.T = T;
+  a.H = d->hidden;
+  a.I = d->inter;
+  a.E = d->n_routed;
+  a.k = d->top_k;
+  a.S = d->n_shared;
+  a.wfmt = d->w_dtype;
+  a.big_start = (int)moe::sched_big_start(r_max, groups(d));
+  a.out_f32 = d->out_dtype == MOE_F32;
+  a.spin_ns = 100000000LL;  // 0.1 s: far beyond any wait of a launch whose blocks are all resident
+  return hip_status(moe::launch_decode_layer(a, stream));
 }
 
 moe_status moe_rmsnorm(int32_t T, int32_t H, float eps, const float* x, void* xn, hipStream_t stream) {

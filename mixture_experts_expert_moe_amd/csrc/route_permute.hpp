@@ -153,6 +153,38 @@ __device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_
   else topk_wave_t<4>(row, E, k, ids, w, ids_copy, s_key, s_sel);
 }
 
+// Ranks of token t's candidates against the keys of one part of its E.
+template <int kPer>
+__device__ __forceinline__ void rank_part(const long long* keys, int E, int lo, int hi, int32_t* above_sum) {
+  const int lane = threadIdx.x % kWave;
+  long long key[kPer];
+  int above[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    key[j] = e < E ? keys[e] : kNoKey;
+    above[j] = 0;
+  }
+  topk_count<kPer>(keys, lo, hi, key, above);
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (lane + kWave * j < E) atomicAdd(&above_sum[lane + kWave * j], above[j]);
+}
+template <int kPer>
+__device__ __forceinline__ void select_token(const float* logit, const int32_t* above_sum, int E, int k, int32_t* ids,
+                                             float* w, int32_t* ids_copy, float* s_sel) {
+  const int lane = threadIdx.x % kWave;
+  float val[kPer];
+  int above[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    val[j] = e < E ? logit[e] : 0.f;
+    above[j] = e < E ? above_sum[e] : k;
+  }
+  topk_select<kPer>(val, above, E, k, ids, w, ids_copy, s_sel);
+}
+
 // Row `row` of src by one block of NT threads: s = max|v| / 127 (IEEE
 // division), q = clamp(rne(v / s), -127, 127); s = 0 gives q = 0.  The block
 // may call this for several rows in turn.
@@ -488,54 +520,65 @@ __device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* 
 }
 
 // The permutation of a few tokens (T <= 16, so every group holds <= 16 rows
-// and is one partial tile) by one block of kPermThreads threads, with the
-// same results as permute_block.  Every (token, expert) pair has a distinct
-// key e * 256 + t, and everything is a count over the keys:
+// and is one partial tile) by one block of NT threads, with the same results
+// as permute_block.  Every (token, expert) pair has a distinct key
+// e * 256 + t, and everything is a count over the keys:
 //   row of (t, e)   = number of keys below its own (rows are grouped by
 //                     expert, token-ascending inside a group);
 //   offsets[g]      = number of keys with expert < g (g <= E), then the
 //                     shared group's T rows;
 //   slot of g's tile = groups with more rows + groups of the same height and
 //                     lower index (per-height counts and group bitmaps).
-// topk_ids may point to global or shared memory.
+// topk_ids and every output may point to global or shared memory.
 constexpr int kFewTokens = 16;
-__device__ __forceinline__ void permute_few_block(const int32_t* topk_ids, int32_t* __restrict__ offsets,
-                                                  int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
-                                                  int32_t* __restrict__ sched, int T, int E, int k, int S,
-                                                  int big_start) {
+template <int NT>
+__device__ __forceinline__ void permute_few_block_t(const int32_t* topk_ids, int32_t* offsets, int32_t* row_token,
+                                                    int32_t* token_row, int32_t* sched, int T, int E, int k, int S,
+                                                    int big_start) {
   constexpr int kMaxPairs = kFewTokens * 16;
   constexpr int kMaskWords = (kMaxGroups + 31) / 32;
-  __shared__ uint32_t s_pkey[kMaxPairs];
+  __shared__ __attribute__((aligned(16))) uint32_t s_pkey[kMaxPairs];
   __shared__ int32_t s_off[kMaxGroups + 1];
   __shared__ int32_t s_hist[kFewTokens + 1];                // groups per height (1..16)
   __shared__ uint32_t s_hmask[kFewTokens + 1][kMaskWords];  // groups of each height
   const int G = E + S, kS = k + S, pairs = T * k;
   const int tid = threadIdx.x;
-  // 1. keys; clear the height tables
-  for (int i = tid; i < pairs; i += kPermThreads) {
-    const int e = topk_ids[i];
+  // 1. keys (padded to a multiple of 4 with keys above every real key); clear the height tables
+  const int pairs4 = (pairs + 3) & ~3;
+  for (int i = tid; i < pairs4; i += NT) {
+    const int e = i < pairs ? topk_ids[i] : -1;
     s_pkey[i] = (unsigned)e < (unsigned)E ? (uint32_t)e * 256u + (uint32_t)(i / k) : 0xffffffffu;
   }
-  for (int i = tid; i < (kFewTokens + 1) * (kMaskWords + 1); i += kPermThreads) {
+  for (int i = tid; i < (kFewTokens + 1) * (kMaskWords + 1); i += NT) {
     if (i < kFewTokens + 1) s_hist[i] = 0;
     else (&s_hmask[0][0])[i - (kFewTokens + 1)] = 0u;
   }
   __syncthreads();
-  // 2. rows of the pairs (threads [0, pairs)) and group offsets (threads from 512)
-  if (tid < pairs) {
-    const uint32_t key = s_pkey[tid];
-    const int t = tid / k, j = tid % k;
+  // 2. rows of the pairs and group offsets (both count over the keys)
+  for (int i = tid; i < pairs; i += NT) {
+    const uint32_t key = s_pkey[i];
+    const int t = i / k, j = i % k;
     int row = -1;
     if (key != 0xffffffffu) {
       row = 0;
-      for (int i = 0; i < pairs; ++i) row += s_pkey[i] < key ? 1 : 0;
+#pragma unroll 4
+      for (int m = 0; m < pairs4; m += 4) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(s_pkey + m);
+        row += (q[0] < key) + (q[1] < key) + (q[2] < key) + (q[3] < key);
+      }
       row_token[row] = t;
     }
     token_row[(size_t)t * kS + j] = row;
-  } else if (tid >= kPermThreads / 2 && tid - kPermThreads / 2 <= E) {
-    const int g = tid - kPermThreads / 2;
+  }
+  // groups go first to the threads past the pairs: g = (tid - pairs) mod NT
+  for (int g = (tid + NT - pairs % NT) % NT; g <= E; g += NT) {
     int off = 0;
-    for (int i = 0; i < pairs; ++i) off += (s_pkey[i] >> 8) < (uint32_t)g ? 1 : 0;
+#pragma unroll 4
+    for (int m = 0; m < pairs4; m += 4) {
+      const u32x4 q = *reinterpret_cast<const u32x4*>(s_pkey + m);
+      off += ((q[0] >> 8) < (uint32_t)g) + ((q[1] >> 8) < (uint32_t)g) + ((q[2] >> 8) < (uint32_t)g) +
+             ((q[3] >> 8) < (uint32_t)g);
+    }
     s_off[g] = off;
     offsets[g] = off;
     if (S && g == E) {
@@ -545,40 +588,49 @@ __device__ __forceinline__ void permute_few_block(const int32_t* topk_ids, int32
   }
   __syncthreads();
   if (S) {
-    for (int t = tid; t < T; t += kPermThreads) {
+    for (int t = tid; t < T; t += NT) {
       const int row = s_off[E] + t;
       token_row[(size_t)t * kS + k] = row;
       row_token[row] = t;
     }
   }
   // 3. heights
-  int n = 0;
-  if (tid < G) {
-    n = s_off[tid + 1] - s_off[tid];
+  for (int g = tid; g < G; g += NT) {
+    const int n = s_off[g + 1] - s_off[g];
     if (n > 0) {
       atomicAdd(&s_hist[n], 1);
-      atomicOr(&s_hmask[n][tid / 32], 1u << (tid % 32));
+      atomicOr(&s_hmask[n][g / 32], 1u << (g % 32));
     }
   }
   __syncthreads();
   // 4. tiles: taller groups first, then lower group index
-  if (tid < G && n > 0) {
+  for (int g = tid; g < G; g += NT) {
+    const int n = s_off[g + 1] - s_off[g];
+    if (n <= 0) continue;
+    // (fixed trip counts, so the LDS reads are all in flight at once)
     int slot = 0;
-    for (int h = n + 1; h <= kFewTokens; ++h) slot += s_hist[h];
-    for (int w = 0; w < tid / 32; ++w) slot += __popc(s_hmask[n][w]);
-    slot += __popc(s_hmask[n][tid / 32] & ((1u << (tid % 32)) - 1u));
+#pragma unroll
+    for (int h = 1; h <= kFewTokens; ++h) slot += h > n ? s_hist[h] : 0;
+#pragma unroll
+    for (int w = 0; w < kMaskWords; ++w) slot += w < g / 32 ? __popc(s_hmask[n][w]) : 0;
+    slot += __popc(s_hmask[n][g / 32] & ((1u << (g % 32)) - 1u));
     int32_t* t4 = sched + kSchedHeader + (size_t)slot * kTileInts;
-    t4[0] = tid;
-    t4[1] = s_off[tid];
+    t4[0] = g;
+    t4[1] = s_off[g];
     t4[2] = n;
     t4[3] = 0;
   }
-  if (tid < kSchedHeader) {
+  for (int i = tid; i < kSchedHeader; i += NT) {
     int tiles = 0;
     for (int h = 1; h <= kFewTokens; ++h) tiles += s_hist[h];
-    sched[tid] = tid == kSchedSmall ? tiles : tid == kSchedGroups ? G : tid == kSchedRows ? s_off[G]
-               : tid == kSchedBigStart ? big_start : 0;
+    sched[i] = i == kSchedSmall ? tiles : i == kSchedGroups ? G : i == kSchedRows ? s_off[G]
+             : i == kSchedBigStart ? big_start : 0;
   }
+}
+__device__ __forceinline__ void permute_few_block(const int32_t* topk_ids, int32_t* offsets, int32_t* row_token,
+                                                  int32_t* token_row, int32_t* sched, int T, int E, int k, int S,
+                                                  int big_start) {
+  permute_few_block_t<kPermThreads>(topk_ids, offsets, row_token, token_row, sched, T, E, k, S, big_start);
 }
 
 }  // namespace moe

@@ -21,38 +21,6 @@ namespace {
 static_assert(kSmallRouteT == kPermWaves, "at least one wave per token");
 static_assert(kSmallRouteT <= kFewTokens, "few-token permutation");
 
-// Ranks of token t's candidates against the keys of one part of its E.
-template <int kPer>
-__device__ __forceinline__ void rank_part(const long long* keys, int E, int lo, int hi, int32_t* above_sum) {
-  const int lane = threadIdx.x % kWave;
-  long long key[kPer];
-  int above[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + kWave * j;
-    key[j] = e < E ? keys[e] : kNoKey;
-    above[j] = 0;
-  }
-  topk_count<kPer>(keys, lo, hi, key, above);
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (lane + kWave * j < E) atomicAdd(&above_sum[lane + kWave * j], above[j]);
-}
-template <int kPer>
-__device__ __forceinline__ void select_token(const float* logit, const int32_t* above_sum, int E, int k, int32_t* ids,
-                                             float* w, int32_t* ids_copy, float* s_sel) {
-  const int lane = threadIdx.x % kWave;
-  float val[kPer];
-  int above[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + kWave * j;
-    val[j] = e < E ? logit[e] : 0.f;
-    above[j] = e < E ? above_sum[e] : k;
-  }
-  topk_select<kPer>(val, above, E, k, ids, w, ids_copy, s_sel);
-}
-
 // Each token gets P = 16 / (the power of two >= T) of the block's 16 waves:
 // they split the key range of its top-k ranks (partial counts summed with
 // LDS atomics, exact in any order) and the columns of its int8 quantisation

@@ -20,8 +20,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 
 # The C-ABI entry points declared in include/moe.h.
 EXPORTS = ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
-           "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_status_string",
-           "moe_abi_version")
+           "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_decode_layer",
+           "moe_status_string", "moe_abi_version")
 
 
 class MoeDesc(ctypes.Structure):
@@ -34,7 +34,9 @@ class MoeWeights(ctypes.Structure):
 
 
 BUFFER_NAMES = ("logits", "topk_ids", "topk_w", "expert_offsets", "row_token", "token_row", "sched", "x_q",
-                "x_scale", "h", "y", "h_q", "h_scale")
+                "x_scale", "h", "y", "h_q", "h_scale", "sync")
+# Word of the sync buffer that a timed-out grid barrier of moe_decode_layer sets.
+SYNC_STATUS_WORD = 640
 
 
 class MoeBuffers(ctypes.Structure):
@@ -67,11 +69,13 @@ def lib():
         L.moe_combine.argtypes = [P(MoeDesc), i32, vp, vp, P(MoeBuffers), vp]
         L.moe_combine_rmsnorm.argtypes = [P(MoeDesc), i32, vp, ctypes.c_float, vp, vp, P(MoeBuffers), vp]
         L.moe_rmsnorm.argtypes = [i32, i32, ctypes.c_float, vp, vp, vp]
+        L.moe_decode_layer.argtypes = [P(MoeDesc), i32, vp, vp, vp, P(MoeWeights), P(MoeWeights), vp, i32,
+                                       ctypes.c_float, vp, P(MoeBuffers), vp]
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
         for f in ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
-                  "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm"):
+                  "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_decode_layer"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -115,7 +119,8 @@ def alloc_buffers(desc: MoeDesc, device="cuda"):
     import torch
     tensors = {}
     for name, nbytes in moe_buffer_sizes(desc).items():
-        tensors[name] = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device) if nbytes else None
+        make = torch.zeros if name == "sync" else torch.empty   # the barrier words start at zero
+        tensors[name] = make(max(nbytes, 16), dtype=torch.uint8, device=device) if nbytes else None
     return tensors, buffers_struct(tensors)
 
 
@@ -161,6 +166,22 @@ def moe_combine_rmsnorm(desc, T, residual, eps, out, xn, bufs: MoeBuffers, strea
                                                             _ptr(xn), ctypes.byref(bufs), _stream(stream)))
 
 
+MOE_DECODE_NORM_INPUT = 1
+
+
+def moe_decode_layer(desc, T, x, w_router, bias, w_gu: MoeWeights, w_down: MoeWeights, residual, flags, eps, out,
+                     bufs: MoeBuffers, stream=None):
+    _check("moe_decode_layer", lib().moe_decode_layer(ctypes.byref(desc), T, _ptr(x), _ptr(w_router), _ptr(bias),
+                                                      ctypes.byref(w_gu), ctypes.byref(w_down), _ptr(residual),
+                                                      flags, eps, _ptr(out), ctypes.byref(bufs), _stream(stream)))
+
+
+def sync_status(tensors: dict) -> int:
+    """Status word of a layer's sync buffer (nonzero: a grid barrier timed out)."""
+    import torch
+    return int(tensors["sync"].view(torch.int32)[SYNC_STATUS_WORD].item())
+
+
 def moe_rmsnorm(T, H, eps, x, xn, stream=None):
     _check("moe_rmsnorm", lib().moe_rmsnorm(T, H, eps, _ptr(x), _ptr(xn), _stream(stream)))
 
@@ -193,6 +214,13 @@ class MoeLayer:
         moe_grouped_gemm_gu(d, T, x, self.gu, self.bufs, stream)
         moe_grouped_gemm_down(d, T, self.dn, self.bufs, stream)
         moe_combine(d, T, residual, out, self.bufs, stream)
+        return out
+
+    def forward_decode(self, x, out, residual=None, norm_input=False, eps=1e-6, stream=None):
+        """The whole layer in one launch (moe_decode_layer, T <= 16); same results as forward().
+        norm_input: x is the fp32 residual stream and out = x + MoE(RMSNorm(x))."""
+        moe_decode_layer(self.desc, x.shape[0], x, self.w["w_router"], self.w.get("bias"), self.gu, self.dn, residual,
+                         MOE_DECODE_NORM_INPUT if norm_input else 0, eps, out, self.bufs, stream)
         return out
 
     def view(self, name, dtype, shape):
@@ -254,4 +282,15 @@ class MoeStack:
             a, b = b, a
         if a.data_ptr() != x.data_ptr():
             x.copy_(a)
+        return x
+
+    def forward_decode(self, x, stream=None):
+        """As forward(), each layer in one launch (moe_decode_layer with the
+        RMSNorm of the residual stream inside, x updated in place; T <= 16):
+        the same bits, one launch per layer instead of four."""
+        T = x.shape[0]
+        d, bf = self.desc, self.bufs
+        for l, w in enumerate(self.layers):
+            moe_decode_layer(d, T, x, w["w_router"], w.get("bias"), self.gu[l], self.dn[l], None,
+                             MOE_DECODE_NORM_INPUT, self.eps, x, bf, stream)
         return x

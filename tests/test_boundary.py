@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 2
+    assert L.moe_abi_version() == 3
 
 
 def test_status_strings():
@@ -65,6 +65,7 @@ def test_buffer_sizes_match_shapes():
     assert s["x_q"] == s["h_q"] == 0
     s8 = moe.moe_buffer_sizes(desc(wt="i8"))
     assert s8["x_q"] == 256 * 2048 and s8["h_q"] == R * 512 and s8["h"] == R * 512 * 4
+    assert s["sync"] == s8["sync"] == 4096
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -75,7 +76,7 @@ def test_buffer_sizes_match_shapes():
     (dict(n_routed=256, max_tokens=1300), -2),
 ])
 def test_bad_desc_rejected(kw, code):
-    sizes = (ctypes.c_size_t * 13)()
+    sizes = (ctypes.c_size_t * 14)()
     assert status("moe_buffer_sizes", ctypes.byref(desc(**kw)), sizes) == code
 
 
@@ -137,3 +138,32 @@ def test_zero_tokens_returns_ok_without_launch():
     assert status("moe_rmsnorm", 0, 2048, ctypes.c_float(1e-6), FAKE, FAKE, None) == 0
     assert status("moe_combine_rmsnorm", by(desc(out="f32")), 0, None, ctypes.c_float(1e-6), FAKE, FAKE, by(b),
                   None) == 0
+
+
+def test_decode_layer_rejects_before_launch():
+    by = ctypes.byref
+    eps = ctypes.c_float(1e-6)
+    w = moe.MoeWeights(FAKE, FAKE, FAKE)
+    b = bufs_all()
+    NORM = moe.MOE_DECODE_NORM_INPUT
+
+    def call(d, T, flags=0, res=None, bufs=b, wts=w, e=eps):
+        return status("moe_decode_layer", by(d), T, FAKE, FAKE, None, by(wts), by(wts), res, flags, e, FAKE,
+                      by(bufs), None)
+    d = desc(max_tokens=32)
+    f32 = desc(max_tokens=32, out="f32")
+    assert call(d, 0) == 0                                   # nothing to do, nothing launched
+    assert call(d, 33) == -3                                 # T > max_tokens
+    assert call(d, 17) == -2                                 # more tokens than one decode launch takes
+    assert call(desc(max_tokens=32, hidden=4096), 9) == -2   # T * hidden > 32768 (inputs kept in LDS)
+    assert call(desc(max_tokens=32, inter=1024), 4) == -2    # staged h rows exceed LDS
+    assert call(desc(max_tokens=32, act="f32", wt="f32", out="f32"), 4) == -2
+    assert call(d, 4, flags=NORM) == -2                      # the residual stream is fp32
+    assert call(f32, 4, flags=NORM, res=FAKE) == -1          # x is the residual in that mode
+    assert call(f32, 4, flags=2) == -1                       # unknown flag
+    assert call(d, 4, e=ctypes.c_float(-1.0)) == -1
+    assert call(d, 4, res=FAKE + 4) == -1
+    assert call(d, 4, bufs=moe.MoeBuffers(*[None if n == "sync" else FAKE for n in moe.BUFFER_NAMES])) == -1
+    assert call(d, 4, wts=moe.MoeWeights(None, None, None)) == -1
+    assert call(desc(max_tokens=32, wt="i8"), 4, bufs=moe.MoeBuffers(
+        *[None if n == "h_q" else FAKE for n in moe.BUFFER_NAMES])) == -1
