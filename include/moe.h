@@ -244,6 +244,22 @@ moe_status moe_decode_layer(const moe_desc* desc, int32_t T, const void* x, cons
                             const moe_weights* w_gu, const moe_weights* w_down, const float* residual,
                             int32_t flags, float eps, void* out, const moe_buffers* bufs, hipStream_t stream);
 
+/* moe_decode_layer for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation and the same bits, with no buffers
+ * argument.  The layer buffers of the call live in a static 8 MiB device
+ * array of the library, which each GPU the library runs on holds until the
+ * process ends; the call allocates nothing.  The desc's max_tokens is
+ * ignored (the array is laid out for 16 tokens); T <= 16, and a desc whose
+ * buffers for 16 tokens exceed 8 MiB returns MOE_ERR_UNSUPPORTED (the layer
+ * shapes of the pages' model, hidden 2048, 128 experts, take about 1.8 MiB).
+ * Every call on one GPU shares that GPU's array and leaves its contents there:
+ * calls that overlap on one GPU (other streams, other threads) race. */
+moe_status moe_decode_layer_static(const moe_desc* desc, int32_t T, const void* x, const void* w_router,
+                                   const float* bias, const moe_weights* w_gu, const moe_weights* w_down,
+                                   const float* residual, int32_t flags, float eps, void* out,
+                                   hipStream_t stream);
+
 /* RMSNorm with unit gain for stacked layers: xn[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)),
  * computed in fp32.  x: [T][H] fp32; xn: [T][H] bf16.  H % 256 == 0. */
 moe_status moe_rmsnorm(int32_t T, int32_t H, float eps, const float* x, void* xn, hipStream_t stream);

@@ -45,6 +45,8 @@
 // a generation word that every block polls.  Every wait is bounded in time: a
 // wait that times out sets the status word of the sync buffer and ends, so the
 // launch always finishes.
+#include <atomic>
+
 #include "gemm_item.hpp"
 #include "route_permute.hpp"
 
@@ -570,6 +572,32 @@ void launch_fmt(const DecodeArgs& a, int nb, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Device memory of the allocation-free decode call (moe_decode_layer_static):
+// the layer buffers of one call, laid out by the caller of
+// decode_static_scratch.  Zero at load, so its barrier words start valid.
+constexpr size_t kStaticScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the host-side name of the array is not a device address).
+hipError_t decode_static_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<void*> cache[kMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = cache[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    cache[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  *bytes = kStaticScratchBytes;
+  return hipSuccess;
+}
 
 int decode_blocks() {
   int dev = 0, cus = 0;

@@ -141,6 +141,9 @@ struct DecodeArgs {
 hipError_t launch_decode_layer(const DecodeArgs& a, hipStream_t stream);
 // Blocks of the decode launch on this device (0 if the device cannot host it).
 int decode_blocks();
+// Device address and size of the static scratch of the allocation-free
+// decode call on the current device.
+hipError_t decode_static_scratch(void** ptr, size_t* bytes);
 // Word of the sync buffer that a timed-out barrier wait sets to nonzero.
 constexpr int kDecodeStatusWord = 64 * 10;
 

@@ -363,6 +363,44 @@ moe_status moe_decode_layer(const moe_desc* d, int32_t T, const void* x, const v
   return hip_status(moe::launch_decode_layer(a, stream));
 }
 
+moe_status moe_decode_layer_static(const moe_desc* d, int32_t T, const void* x, const void* w_router,
+                                   const float* bias, const moe_weights* w_gu, const moe_weights* w_down,
+                                   const float* residual, int32_t flags, float eps, void* out,
+                                   hipStream_t stream) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  moe_desc ds = *d;  // the layout of the static buffers: room for kDecodeMaxT tokens
+  ds.max_tokens = moe::kDecodeMaxT;
+  moe_status s = check_desc(&ds);
+  if (s != MOE_OK) return s;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > moe::kDecodeMaxT) return MOE_ERR_UNSUPPORTED;
+  size_t sizes[MOE_NUM_BUFFERS];
+  if ((s = moe_buffer_sizes(&ds, sizes)) != MOE_OK) return s;
+  if (T == 0) {  // the other arguments are still checked; nothing touches the device
+    void* const fake = (void*)(uintptr_t)256;
+    const moe_buffers b0{(float*)fake, (int32_t*)fake, (float*)fake, (int32_t*)fake, (int32_t*)fake,
+                         (int32_t*)fake, (int32_t*)fake, (int8_t*)fake, (float*)fake, fake, fake, (int8_t*)fake,
+                         (float*)fake, (uint32_t*)fake};
+    return moe_decode_layer(&ds, 0, x, w_router, bias, w_gu, w_down, residual, flags, eps, out, &b0, stream);
+  }
+  size_t total = 0;
+  for (size_t z : sizes) total += (z + 255) / 256 * 256;
+  void* base = nullptr;
+  size_t cap = 0;
+  if (moe::decode_static_scratch(&base, &cap) != hipSuccess) return MOE_ERR_HIP;
+  if (total > cap) return MOE_ERR_UNSUPPORTED;
+  void* p[MOE_NUM_BUFFERS];
+  size_t off = 0;
+  for (int i = 0; i < MOE_NUM_BUFFERS; ++i) {
+    p[i] = sizes[i] ? (void*)((char*)base + off) : nullptr;
+    off += (sizes[i] + 255) / 256 * 256;
+  }
+  const moe_buffers b{(float*)p[0], (int32_t*)p[1], (float*)p[2], (int32_t*)p[3], (int32_t*)p[4], (int32_t*)p[5],
+                      (int32_t*)p[6], (int8_t*)p[7], (float*)p[8], p[9], p[10], (int8_t*)p[11], (float*)p[12],
+                      (uint32_t*)p[13]};
+  return moe_decode_layer(&ds, T, x, w_router, bias, w_gu, w_down, residual, flags, eps, out, &b, stream);
+}
+
 moe_status moe_rmsnorm(int32_t T, int32_t H, float eps, const float* x, void* xn, hipStream_t stream) {
   if (T < 0 || H <= 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   if (H % 256) return MOE_ERR_UNSUPPORTED;

@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 # The C-ABI entry points declared in include/moe.h.
 EXPORTS = ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
            "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_decode_layer",
-           "moe_status_string", "moe_abi_version")
+           "moe_decode_layer_static", "moe_status_string", "moe_abi_version")
 
 
 class MoeDesc(ctypes.Structure):
@@ -71,11 +71,14 @@ def lib():
         L.moe_rmsnorm.argtypes = [i32, i32, ctypes.c_float, vp, vp, vp]
         L.moe_decode_layer.argtypes = [P(MoeDesc), i32, vp, vp, vp, P(MoeWeights), P(MoeWeights), vp, i32,
                                        ctypes.c_float, vp, P(MoeBuffers), vp]
+        L.moe_decode_layer_static.argtypes = [P(MoeDesc), i32, vp, vp, vp, P(MoeWeights), P(MoeWeights), vp, i32,
+                                              ctypes.c_float, vp, vp]
         L.moe_status_string.argtypes = [i32]
         L.moe_status_string.restype = ctypes.c_char_p
         L.moe_abi_version.restype = i32
         for f in ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
-                  "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_decode_layer"):
+                  "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_decode_layer",
+                  "moe_decode_layer_static"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -174,6 +177,14 @@ def moe_decode_layer(desc, T, x, w_router, bias, w_gu: MoeWeights, w_down: MoeWe
     _check("moe_decode_layer", lib().moe_decode_layer(ctypes.byref(desc), T, _ptr(x), _ptr(w_router), _ptr(bias),
                                                       ctypes.byref(w_gu), ctypes.byref(w_down), _ptr(residual),
                                                       flags, eps, _ptr(out), ctypes.byref(bufs), _stream(stream)))
+
+
+def moe_decode_layer_static(desc, T, x, w_router, bias, w_gu: MoeWeights, w_down: MoeWeights, residual, flags, eps,
+                            out, stream=None):
+    _check("moe_decode_layer_static",
+           lib().moe_decode_layer_static(ctypes.byref(desc), T, _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(w_gu),
+                                         ctypes.byref(w_down), _ptr(residual), flags, eps, _ptr(out),
+                                         _stream(stream)))
 
 
 def sync_status(tensors: dict) -> int:

@@ -167,3 +167,20 @@ def test_decode_layer_rejects_before_launch():
     assert call(d, 4, wts=moe.MoeWeights(None, None, None)) == -1
     assert call(desc(max_tokens=32, wt="i8"), 4, bufs=moe.MoeBuffers(
         *[None if n == "h_q" else FAKE for n in moe.BUFFER_NAMES])) == -1
+
+
+def test_decode_layer_static_rejects_before_launch():
+    by = ctypes.byref
+    eps = ctypes.c_float(1e-6)
+    w = moe.MoeWeights(FAKE, FAKE, FAKE)
+
+    def call(d, T, x=FAKE, flags=0):
+        return status("moe_decode_layer_static", by(d) if d is not None else None, T, x, FAKE, None, by(w), by(w),
+                      None, flags, eps, FAKE, None)
+    d = desc(max_tokens=4)
+    assert call(d, 0) == 0                      # nothing to do; the device is not touched
+    assert call(d, 0, x=None) == -1             # arguments are checked even then
+    assert call(None, 1) == -1
+    assert call(d, -1) == -1
+    assert call(d, 17) == -2                    # the static buffers are laid out for 16 tokens
+    assert call(desc(hidden=2000), 1) == -2
