@@ -114,20 +114,45 @@ __device__ void grid_barrier(uint32_t* sync, int per_xcd, long long spin_ns) {
 // this XCD's L2).  As ordinary loads to the compiler they are issued back to
 // back, where agent-scope atomic loads would each wait for the one before.
 // Word 3 of the resource is the raw-buffer format of the gfx9 family;
-// offsets past num_records bytes read as zero.
-struct CohBuf {
+// offsets past num_records bytes read as zero, so a load that may not be
+// needed is issued anyway at kNoOffset rather than behind a branch (a load
+// in a branch gets a full wait in front of it).
+constexpr uint32_t kNoOffset = 0xfffffff0u;
+template <int kAux>  // cache policy bits: 16 = sc1 (coherent), 0 = plain
+struct BufLd {
   __amdgpu_buffer_rsrc_t r;
-  __device__ CohBuf(const void* base, uint32_t bytes)
+  __device__ BufLd(const void* base, uint32_t bytes)
       : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000)) {}
   __device__ uint64_t ld64(uint32_t byte_off) const {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, 16);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)byte_off, 0, kAux);
     return ((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0];
   }
   __device__ u32x4 ld128(uint32_t byte_off) const {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 16);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, kAux);
     return u32x4{(uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]};
   }
 };
+using CohBuf = BufLd<16>;
+
+// Sum over the wave of an fp64 value with DPP lane moves (the wave-scan
+// pattern of route_permute.hpp on both 32-bit halves): row shifts by 1, 2, 4,
+// 8, then the row broadcasts of lanes 15 and 31; the total lands in lane 63.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(b & 0xffffffffll), kCtrl, kRowMask, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), kCtrl, kRowMask, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+__device__ __forceinline__ double wave_sum_f64_last(double v) {
+  v += dpp_f64<kDppShr1, 0xf>(v);
+  v += dpp_f64<kDppShr2, 0xf>(v);
+  v += dpp_f64<kDppShr4, 0xf>(v);
+  v += dpp_f64<kDppShr8, 0xf>(v);
+  v += dpp_f64<kDppBcast15, 0xa>(v);
+  v += dpp_f64<kDppBcast31, 0xc>(v);
+  return v;
+}
 
 __device__ __forceinline__ void bf16x8_to_f32(const u32x4& a, float v[8]) {
 #pragma unroll
@@ -238,32 +263,15 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
       __syncthreads();  // L.part is reused by the next pair of tokens
     }
   } else {
-    for (int c = 8 * tid; c < T * H; c += 8 * kThreads)
-      *reinterpret_cast<u32x4*>(xin + c) = ld16((const uint16_t*)a.x + c);
+    constexpr int kChunks = kDecodeMaxTH / (8 * kThreads);  // 16-byte chunks per thread, all loaded first
+    const BufLd<0> xbuf(a.x, (uint32_t)(T * H * 2));
+    u32x4 v[kChunks];
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j) v[j] = xbuf.ld128((uint32_t)(tid + j * kThreads) * 16);
+#pragma unroll
+    for (int j = 0; j < kChunks; ++j)
+      if (8 * (tid + j * kThreads) < T * H) *reinterpret_cast<u32x4*>(xin + 8 * (tid + j * kThreads)) = v[j];
     __syncthreads();
-  }
-  if constexpr (WF == kI8) {
-    // per-token codes of the int8 path: wave w quantises tokens w and w + 8
-    for (int t = wave; t < T; t += kWaves) {
-      const uint16_t* row = xin + (size_t)t * H;
-      float amax = 0.f;
-      for (int c = 8 * lane; c < H; c += 8 * kWave) {
-        float v[8];
-        bf16x8_to_f32(*reinterpret_cast<const u32x4*>(row + c), v);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-      }
-      const float s = __fdiv_rn(wave_max_dpp(amax), 127.0f);
-      for (int c = 8 * lane; c < H; c += 8 * kWave) {
-        float v[8];
-        bf16x8_to_f32(*reinterpret_cast<const u32x4*>(row + c), v);
-        uint32_t pk[2] = {0u, 0u};
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pk[j / 4] |= (uint32_t)(uint8_t)(int8_t)quant_i8(v[j], s) << (8 * (j % 4));
-        *reinterpret_cast<u32x2*>(L.act + (size_t)t * H + c) = u32x2{pk[0], pk[1]};
-      }
-      if (lane == 0) L.x_scale[t] = s;
-    }
   }
   // router: unit u = (expert u / ns, slice u % ns of H), 8-value chunks per thread
   for (int u = blockIdx.x; u < E * ns; u += NB) {
@@ -288,10 +296,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
 #pragma unroll
     for (int t = 0; t < kDecodeMaxT; ++t) {
       if (t < T) {
-        double v = acc[t];
-#pragma unroll
-        for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
-        if (lane == 0) L.u.p0.red64[wave * kDecodeMaxT + t] = v;
+        const double v = wave_sum_f64_last(acc[t]);
+        if (lane == kWave - 1) L.u.p0.red64[wave * kDecodeMaxT + t] = v;
       }
     }
     __syncthreads();
@@ -302,20 +308,65 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
     }
     __syncthreads();
   }
-  if constexpr (WF == kI8) {
-    if (lead) {
-      for (int i = tid; i < T * H / 8; i += kThreads)
-        reinterpret_cast<u32x2*>(a.x_q)[i] = reinterpret_cast<const u32x2*>(L.act)[i];
-      if (tid < T) a.x_scale[tid] = L.x_scale[tid];
+  {
+    // the int8 codes are only needed from P2 on: they are made while this
+    // block waits at the barrier
+    const uint32_t g0 = grid_arrive(a.sync, per_xcd);
+    if constexpr (WF == kI8) {
+      // per-token codes of the int8 path: token t gets P = 8 / (the power of
+      // two >= T) waves (one wave per token from 8 tokens on), which split its
+      // columns; their maxima meet in LDS (max is exact in any order)
+      const int P = T <= 1 ? 8 : T <= 2 ? 4 : T <= 4 ? 2 : 1;
+      float* s_max = reinterpret_cast<float*>(L.u.p0.red64);  // [waves] (red64 is not in use yet)
+      for (int t0 = 0; t0 < T; t0 += kWaves / P) {
+        const int t = t0 + wave / P, part = wave % P, cw = H / P;
+        const uint16_t* row = xin + (size_t)t * H + part * cw;
+        float amax = 0.f;
+        if (t < T)
+          for (int c = 8 * lane; c < cw; c += 8 * kWave) {
+            float v[8];
+            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(row + c), v);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+          }
+        amax = wave_max_dpp(amax);
+        if (lane == 0) s_max[wave] = amax;
+        __syncthreads();
+        if (t < T) {
+          float m = 0.f;
+          for (int w = 0; w < P; ++w) m = fmaxf(m, s_max[(wave / P) * P + w]);
+          const float s = __fdiv_rn(m, 127.0f);
+          for (int c = 8 * lane; c < cw; c += 8 * kWave) {
+            float v[8];
+            bf16x8_to_f32(*reinterpret_cast<const u32x4*>(row + c), v);
+            uint32_t pk[2] = {0u, 0u};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) pk[j / 4] |= (uint32_t)(uint8_t)(int8_t)quant_i8(v[j], s) << (8 * (j % 4));
+            *reinterpret_cast<u32x2*>(L.act + (size_t)t * H + part * cw + c) = u32x2{pk[0], pk[1]};
+          }
+          if (lane == 0 && part == 0) L.x_scale[t] = s;
+        }
+        __syncthreads();  // s_max is reused by the next tokens
+      }
     }
+    if constexpr (WF == kI8) {
+      if (lead) {
+        for (int i = tid; i < T * H / 8; i += kThreads)
+          reinterpret_cast<u32x2*>(a.x_q)[i] = reinterpret_cast<const u32x2*>(L.act)[i];
+        if (tid < T) a.x_scale[tid] = L.x_scale[tid];
+      }
+    }
+    grid_wait(a.sync, g0, a.spin_ns);
   }
-  grid_barrier(a.sync, per_xcd, a.spin_ns);
 
   // ---- P1: logits, top-k, permutation (every block, in LDS) ---------------------
   const CohBuf pbuf(a.partials, (uint32_t)(ns * T * E * 8));
   for (int i = tid; i < T * E; i += kThreads) {
-    double s = __longlong_as_double((long long)pbuf.ld64(i * 8));
-    for (int sl = 1; sl < ns; ++sl) s += __longlong_as_double((long long)pbuf.ld64((sl * T * E + i) * 8));
+    uint64_t part[kRouteSlices];
+#pragma unroll
+    for (int sl = 0; sl < kRouteSlices; ++sl) part[sl] = pbuf.ld64(sl < ns ? (uint32_t)(sl * T * E + i) * 8 : kNoOffset);
+    double s = __longlong_as_double((long long)part[0]);
+    for (int sl = 1; sl < ns; ++sl) s += __longlong_as_double((long long)part[sl]);
     float v = (float)s;
     if (a.bias) v = __fadd_rn(v, a.bias[i % E]);
     L.u.route.logit[i] = v;
@@ -458,10 +509,8 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
               const int c = 4 * lane + 4 * kWave * j;
-              if (c < I) {
-                v[j][0] = hbuf.ld64(src + 4 * c);
-                v[j][1] = hbuf.ld64(src + 4 * c + 8);
-              }
+              v[j][0] = hbuf.ld64(c < I ? src + 4 * c : kNoOffset);
+              v[j][1] = hbuf.ld64(c < I ? src + 4 * c + 8 : kNoOffset);
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
@@ -510,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
     const int upt = H / 256, n_units = T * upt;
     const CohBuf ybuf(a.y, (uint32_t)(R * H * (kF32Out ? 4 : 2)));
     const float* res = kNormIn ? (const float*)a.x : a.residual;
-    for (int u = blockIdx.x * kWaves + wave; u < n_units; u += NB * kWaves) {
+    for (int u = wave * NB + (int)blockIdx.x; u < n_units; u += NB * kWaves) {
       const int t = u / upt, c = (u % upt) * 256 + 4 * lane;
       constexpr int kGroup = 9;  // rows loaded together before the first is used
       float acc[4] = {0.f, 0.f, 0.f, 0.f}, rv[4];
@@ -524,19 +573,17 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
 #pragma unroll
         for (int j = 0; j < kGroup; ++j) {
           const int r = j0 + j < kS ? L.token_row[t * kS + j0 + j] : -1;
-          if (r >= 0) {
-            if constexpr (kF32Out) {
-              const u32x4 q = ybuf.ld128((uint32_t)(r * H + c) * 4);
+          if constexpr (kF32Out) {
+            const u32x4 q = ybuf.ld128(r >= 0 ? (uint32_t)(r * H + c) * 4 : kNoOffset);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) yv[j][i] = __uint_as_float(q[i]);
-            } else {
-              const uint64_t q = ybuf.ld64((uint32_t)(r * H + c) * 2);
-              const uint32_t lo = (uint32_t)q, hi = (uint32_t)(q >> 32);
-              yv[j][0] = __uint_as_float(lo << 16);
-              yv[j][1] = __uint_as_float(lo & 0xffff0000u);
-              yv[j][2] = __uint_as_float(hi << 16);
-              yv[j][3] = __uint_as_float(hi & 0xffff0000u);
-            }
+            for (int i = 0; i < 4; ++i) yv[j][i] = __uint_as_float(q[i]);
+          } else {
+            const uint64_t q = ybuf.ld64(r >= 0 ? (uint32_t)(r * H + c) * 2 : kNoOffset);
+            const uint32_t lo = (uint32_t)q, hi = (uint32_t)(q >> 32);
+            yv[j][0] = __uint_as_float(lo << 16);
+            yv[j][1] = __uint_as_float(lo & 0xffff0000u);
+            yv[j][2] = __uint_as_float(hi << 16);
+            yv[j][3] = __uint_as_float(hi & 0xffff0000u);
           }
         }
 #pragma unroll
