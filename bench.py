@@ -86,6 +86,11 @@ def load_traffic(kernel, workload, launch_algo_bytes):
     return rec.get("hbm_bytes_per_launch")
 
 
+def synth_spec(name):
+    from gen import synth
+    return synth.workload(name).spec
+
+
 class Runner:
     """Device-resident inputs of one workload and its MoeLayer."""
 
@@ -326,6 +331,9 @@ def main():
     ap.add_argument("--no-fp32", action="store_true", help="skip the fp32 16-expert figure")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer 4-bit stack figures")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
+    ap.add_argument("--workloads", default="headline,decode,fp32,q4,stack",
+                    help="comma list of the parts to run (profiling runs pick one); without 'headline' the line's "
+                         "value is null")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a reference kernel of known "
                          "size for hardware-counter calibration)")
@@ -335,6 +343,13 @@ def main():
         print("bench.py measures one GPU only: this layer is built and measured on a single MI355X "
               "(no sharding, no collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    parts = set(args.workloads.split(","))
+    args.no_decode = args.no_decode or "decode" not in parts
+    args.no_fp32 = args.no_fp32 or "fp32" not in parts
+    args.no_q4 = args.no_q4 or "q4" not in parts
+    args.no_stack = args.no_stack or "stack" not in parts
+    headline = "headline" in parts
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -351,33 +366,35 @@ def main():
         del src, dst
 
     name, T = "bf16_e128_top8_shared", 256
-    r = Runner(name, T, args.rotations, args.steps + args.warmup)
-    wall, U, kms = r.timed(args.steps, args.warmup)
-    ms = wall / args.steps * 1e3
-    value = T / (ms / 1e3)
-    spec = r.spec
-    gu_bytes = gu_algorithmic_bytes(spec, T, U)
-    gu_ms = kms["gate_up"]
-    achieved = gu_bytes / (gu_ms / 1e3) / 1e9
-    dn_bytes = down_algorithmic_bytes(spec, T, U)
-    R = T * (spec.top_k + spec.n_shared)
-    flops = 2.0 * R * (2 * spec.inter * spec.hidden + spec.hidden * spec.inter)
-    traffic = load_traffic("gate_up", name, gu_bytes)
-    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "kernel": "grouped_gemm_kernel<bf16, gate_up>", "algorithmic_bytes_per_launch": gu_bytes,
-                "avg_launch_ms": round(gu_ms, 5)}
-    extra = {
-        "kernel_ms": {k: round(v, 5) for k, v in kms.items()},
-        "touched_groups": U,
-        "down_hbm_frac": round(dn_bytes / (kms["down"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-        "gemm_mfma_frac_bf16": round(flops / ((kms["gate_up"] + kms["down"]) / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
-                                     4),
-        "layer_hbm_frac": round((gu_bytes + dn_bytes) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-        "weight_sets_rotated": args.rotations,
-    }
-    del r
-    torch.cuda.empty_cache()
+    value = ms = roofline = None
+    extra = {"weight_sets_rotated": args.rotations}
+    spec = synth_spec(name)
+    if headline:
+        r = Runner(name, T, args.rotations, args.steps + args.warmup)
+        wall, U, kms = r.timed(args.steps, args.warmup)
+        ms = wall / args.steps * 1e3
+        value = T / (ms / 1e3)
+        gu_bytes = gu_algorithmic_bytes(spec, T, U)
+        gu_ms = kms["gate_up"]
+        achieved = gu_bytes / (gu_ms / 1e3) / 1e9
+        dn_bytes = down_algorithmic_bytes(spec, T, U)
+        R = T * (spec.top_k + spec.n_shared)
+        flops = 2.0 * R * (2 * spec.inter * spec.hidden + spec.hidden * spec.inter)
+        traffic = load_traffic("gate_up", name, gu_bytes)
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                    "kernel": "grouped_gemm_kernel<bf16, gate_up>", "algorithmic_bytes_per_launch": gu_bytes,
+                    "avg_launch_ms": round(gu_ms, 5)}
+        extra.update({
+            "kernel_ms": {k: round(v, 5) for k, v in kms.items()},
+            "touched_groups": U,
+            "down_hbm_frac": round(dn_bytes / (kms["down"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemm_mfma_frac_bf16": round(flops / ((kms["gate_up"] + kms["down"]) / 1e3) / 1e12
+                                         / MFMA_BF16_PEAK_TFLOPS, 4),
+            "layer_hbm_frac": round((gu_bytes + dn_bytes) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        })
+        del r
+        torch.cuda.empty_cache()
 
     if not args.no_decode:
         sweep, fsweep = {}, {}
@@ -441,15 +458,16 @@ def main():
         torch.cuda.empty_cache()
 
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "metric": METRIC, "value": round(value, 1) if value else None, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5) if ms else None,
+        "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "tokens": T, "hidden": spec.hidden, "inter": spec.inter,
                    "routed_experts": spec.n_routed, "top_k": spec.top_k, "shared_experts": spec.n_shared,
                    "weights": spec.wt, "parallelism": "none (one GPU)"},
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and headline:
         line["cpu_baseline"] = cpu_baseline(name, T, min(args.cpu_sample, T))
     line["extra"] = extra
     print(json.dumps(line), flush=True)

@@ -225,6 +225,62 @@ void synth_weights_q4(uint64_t key, int32_t G, int32_t n, int32_t k, float std_,
   });
 }
 
+// G matrices [n][k] of N(0, std) in MXFP4 blocks of 32 consecutive k (the OCP
+// microscaling format, Open Compute Project "OCP Microscaling Formats (MX)
+// v1.0"): one E8M0 scale byte per block (value 2^(byte - 127)) and 4-bit E2M1
+// elements (sign, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6).  Per block:
+//   amax = max |w|; amax == 0 gives scale byte 0 and all codes 0; otherwise
+//   byte = clamp(floor(log2(amax)) - 2 + 127, 0, 254)   (2 = the exponent of 6),
+//   code = the E2M1 value nearest to w / 2^(byte - 127), ties to the even
+//          mantissa, magnitudes above 6 saturated to 6.
+// Packing: byte b of a block holds element 2b in the low nibble, 2b+1 in the high one.
+// Layouts: packed [G][n][k/2] bytes, scales [G][n][k/32] bytes.
+namespace {
+uint32_t e2m1_code(float v) {
+  static const float kMag[8] = {0.f, 0.5f, 1.f, 1.5f, 2.f, 3.f, 4.f, 6.f};
+  const float a = std::fabs(v);
+  int best = 0;
+  for (int c = 1; c < 8; ++c) {
+    const float d = std::fabs(a - kMag[c]), db = std::fabs(a - kMag[best]);
+    if (d < db || (d == db && (c & 1) == 0)) best = c;  // ties to the even mantissa bit
+  }
+  if (a > 6.f) best = 7;
+  return best == 0 ? 0u : (uint32_t)best | (v < 0.f ? 8u : 0u);
+}
+}  // namespace
+void synth_weights_mx4(uint64_t key, int32_t G, int32_t n, int32_t k, float std_, uint8_t* packed,
+                       uint8_t* scales, int threads) {
+  const int64_t rows = (int64_t)G * n;
+  const int32_t nb = k / 32;
+  parallel_for(rows, threads, [&](int64_t lo, int64_t hi) {
+    for (int64_t r = lo; r < hi; ++r) {
+      const int64_t g = r / n, row = r % n;
+      const uint64_t kg = synth_mix(key, (uint64_t)g);
+      for (int32_t b = 0; b < nb; ++b) {
+        float w[32];
+        fill_values(kg, row * (int64_t)k + b * 32, 32, 0.f, std_, w);
+        float amax = 0.f;
+        for (int j = 0; j < 32; ++j) amax = std::max(amax, std::fabs(w[j]));
+        int byte = 0;
+        if (amax > 0.f) {
+          int ex;
+          std::frexp(amax, &ex);  // amax = m 2^ex, m in [0.5, 1): floor(log2(amax)) = ex - 1
+          byte = std::min(254, std::max(0, ex - 1 - 2 + 127));
+        }
+        scales[r * nb + b] = (uint8_t)byte;
+        const float inv = (float)std::ldexp(1.0, 127 - byte);  // 1 / 2^(byte - 127), exact
+        uint8_t* dst = packed + r * (int64_t)(k / 2) + b * 16;
+        for (int j = 0; j < 16; ++j) {
+          const uint32_t lo4 = amax > 0.f ? e2m1_code(w[2 * j] * inv) : 0u;
+          const uint32_t hi4 = amax > 0.f ? e2m1_code(w[2 * j + 1] * inv) : 0u;
+          dst[j] = (uint8_t)(lo4 | (hi4 << 4));
+        }
+      }
+    }
+  });
+}
+
 // G matrices [n][k] of N(0, std) as fp32 or bf16 (matrix g uses key synth_mix(key, g)).
 void synth_weights_f32(uint64_t key, int32_t G, int32_t n, int32_t k, float std_, float* out, int threads) {
   parallel_for((int64_t)G * n, threads, [&](int64_t lo, int64_t hi) {

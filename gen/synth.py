@@ -58,6 +58,7 @@ def lib():
         L.synth_weights_bf16.argtypes = [u64, i32, i32, i32, f32, p, ctypes.c_int]
         L.synth_weights_i8.argtypes = [u64, i32, i32, i32, f32, p, p, ctypes.c_int]
         L.synth_weights_q4.argtypes = [u64, i32, i32, i32, f32, p, p, p, ctypes.c_int]
+        L.synth_weights_mx4.argtypes = [u64, i32, i32, i32, f32, p, p, ctypes.c_int]
         L.synth_permutation.argtypes = [u64, i32, p]
         L.synth_zipf_bias.argtypes = [u64, i32, ctypes.c_double, p]
         _lib = L
@@ -100,7 +101,8 @@ def weights(k: int, G: int, n: int, kdim: int, std: float, fmt: str) -> dict:
     """G expert matrices [n][kdim] (K contiguous) of N(0, std) in a storage format.
 
     fmt "f32": {"w": float32}; "bf16": {"w": uint16 bits}; "i8": {"w": int8, "scale": float32 [G][n]};
-    "q4": {"w": uint8 [G][n][kdim/2], "scale": uint16 fp16 [G][n][kdim/32], "min": same}.
+    "q4": {"w": uint8 [G][n][kdim/2], "scale": uint16 fp16 [G][n][kdim/32], "min": same};
+    "mx4": {"w": uint8 [G][n][kdim/2] E2M1 pairs, "scale": uint8 E8M0 [G][n][kdim/32]}.
     """
     L, t = lib(), _threads()
     if fmt == "f32":
@@ -124,6 +126,13 @@ def weights(k: int, G: int, n: int, kdim: int, std: float, fmt: str) -> dict:
         m = np.empty((G, n, kdim // 32), np.uint16)
         L.synth_weights_q4(k, G, n, kdim, std, _ptr(w), _ptr(s), _ptr(m), t)
         return {"w": w, "scale": s, "min": m}
+    if fmt == "mx4":
+        if kdim % 32:
+            raise ValueError("MXFP4 blocks need K % 32 == 0")
+        w = np.empty((G, n, kdim // 2), np.uint8)
+        s = np.empty((G, n, kdim // 32), np.uint8)
+        L.synth_weights_mx4(k, G, n, kdim, std, _ptr(w), _ptr(s), t)
+        return {"w": w, "scale": s}
     raise ValueError(fmt)
 
 
@@ -148,7 +157,7 @@ class LayerSpec:
     top_k: int = 8
     n_shared: int = 1
     act: str = "bf16"      # x and router weight: "f32" | "bf16"
-    wt: str = "bf16"       # expert weights: "f32" | "bf16" | "i8" | "q4"
+    wt: str = "bf16"       # expert weights: "f32" | "bf16" | "i8" | "q4" | "mx4"
     out: str = "bf16"      # layer output: "f32" | "bf16"
     zipf: float = 0.0      # Zipf exponent of the per-expert router bias; 0 = no bias
     w_std: float = 0.02
@@ -183,6 +192,13 @@ WORKLOADS = {
                                notes="40 MoE layers with RMSNorm and residual; 2600-token prompt in 256-token chunks, "
                                      "then 64 single-token decode steps",
                                extra={"prompt": 2600, "chunk": 256, "decode_steps": 64, "eps": 1e-6})),
+    "mx4_e128_top8_shared_zipf": (6, Workload("mx4_e128_top8_shared_zipf", LayerSpec(wt="mx4", zipf=1.1),
+                                              tokens=(2048,),
+                                              notes="MXFP4 expert weights with MXFP8 activations, Zipf(1.1) router "
+                                                    "bias, 2048-token prefill")),
+    "mx4_e128_top8_shared": (7, Workload("mx4_e128_top8_shared", LayerSpec(wt="mx4"), tokens=(1, 2, 4, 8, 256),
+                                         notes="MXFP4 expert weights with MXFP8 activations, decode rows and a "
+                                               "256-token chunk")),
 }
 
 

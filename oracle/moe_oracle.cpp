@@ -49,7 +49,7 @@
 
 namespace {
 
-enum Dtype { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2, DT_Q4 = 3 };
+enum Dtype { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2, DT_Q4 = 3, DT_MX4 = 4 };
 
 // ---- number formats (the oracle's own decoders) ---------------------------
 
@@ -88,6 +88,74 @@ double round_bf16_d(double d) {
   return std::ldexp(std::nearbyint(std::ldexp(m, 8)), e - 8);
 }
 
+// ---- OCP microscaling (MX) formats ------------------------------------------
+// A block of 32 values shares one E8M0 scale byte s, worth 2^(s - 127).
+double e8m0_value(uint8_t s) { return std::ldexp(1.0, (int)s - 127); }
+
+// E2M1 element (4 bits): sign, 2 exponent bits (bias 1), 1 mantissa bit;
+// exponent 0 is subnormal (mantissa x 0.5).
+double e2m1_value(int code) {
+  const int sign = (code >> 3) & 1, e = (code >> 1) & 3, m = code & 1;
+  const double mag = e == 0 ? 0.5 * m : std::ldexp(1.0 + 0.5 * m, e - 1);
+  return sign ? -mag : mag;
+}
+
+// E4M3 element (OCP "E4M3", no infinities): sign, 4 exponent bits (bias 7),
+// 3 mantissa bits; exponent 0 is subnormal (mantissa x 2^-9); largest 448.
+double e4m3_value(int code) {
+  const int sign = (code >> 7) & 1, e = (code >> 3) & 15, m = code & 7;
+  const double mag = e == 0 ? std::ldexp((double)m, -9) : std::ldexp(8.0 + m, e - 10);
+  return sign ? -mag : mag;
+}
+
+// The E4M3 value nearest to a >= 0 (ties to the even mantissa), magnitudes
+// above 448 saturated to 448: a rounded to a multiple of 2^(max(E, -6) - 3),
+// E = floor(log2(a)), which is the spacing of E4M3 values at a.
+double e4m3_round(double a) {
+  if (a == 0.0) return 0.0;
+  int ex;
+  std::frexp(a, &ex);  // a = m 2^ex, m in [0.5, 1)
+  const int q = std::max(ex - 1, -6) - 3;
+  const double r = std::ldexp(std::nearbyint(std::ldexp(a, -q)), q);
+  return std::min(r, 448.0);
+}
+int e4m3_code(double r, bool neg) {  // r: a value e4m3_round returned
+  int code;
+  if (r == 0.0) return 0;
+  int ex;
+  std::frexp(r, &ex);
+  const int E = ex - 1;
+  if (E >= -6) code = ((E + 7) << 3) | (int)(std::ldexp(r, 3 - E) - 8.0);
+  else code = (int)std::ldexp(r, 9);
+  return code | (neg ? 0x80 : 0);
+}
+
+// MXFP8 (E4M3) quantisation of one row in blocks of 32 (the OCP MX
+// conversion): amax = max |v| of the block; amax == 0 gives scale byte 0 and
+// codes 0; otherwise scale byte = clamp(floor(log2(amax)) - 8 + 127, 0, 254)
+// (8 = the exponent of 448), code = e4m3(v / scale).  deq receives the value
+// each code stands for (code value x scale).
+void quant_mx8_row(int cols, const float* v, uint8_t* codes, uint8_t* scales, double* deq) {
+  for (int b = 0; b < cols / 32; ++b) {
+    double amax = 0.0;
+    for (int j = 0; j < 32; ++j) amax = std::max(amax, std::fabs((double)v[b * 32 + j]));
+    int s = 0;
+    if (amax > 0.0) {
+      int ex;
+      std::frexp(amax, &ex);
+      s = std::min(254, std::max(0, ex - 1 - 8 + 127));
+    }
+    scales[b] = (uint8_t)s;
+    for (int j = 0; j < 32; ++j) {
+      const double x = (double)v[b * 32 + j];
+      int c = 0;
+      if (amax > 0.0) c = e4m3_code(e4m3_round(std::ldexp(std::fabs(x), 127 - s)), x < 0.0);
+      codes[b * 32 + j] = (uint8_t)c;
+      deq[b * 32 + j] = e4m3_value(c) * e8m0_value((uint8_t)s);
+    }
+  }
+}
+
 double act_value(int dt, const void* x, int64_t i) {
   if (dt == DT_F32) return ((const float*)x)[i];
   return bf16_value(((const uint16_t*)x)[i]);
@@ -115,6 +183,12 @@ struct Weights {
         const float m = f16_value(((const uint16_t*)mn)[b]);
         const float v = s * (float)q + m;  // s*q is exact in fp32; one rounding in the add
         return round_bf16(v);
+      }
+      case DT_MX4: {
+        const uint8_t byte = ((const uint8_t*)w)[i / 2];
+        const int code = (k & 1) ? (byte >> 4) : (byte & 15);
+        const int64_t b = ((int64_t)g * N + n) * (K / 32) + k / 32;
+        return e2m1_value(code) * e8m0_value(((const uint8_t*)scale)[b]);
       }
     }
     return NAN;
@@ -276,7 +350,14 @@ int oracle_gu(int T, int H, int I, int G, const int32_t* offsets, const int32_t*
     parallel_for(r1 - r0, threads, [&](int64_t rr) {
       const int r = r0 + (int)rr, t = row_token[r];
       std::vector<double> xr((size_t)H);
-      for (int c = 0; c < H; ++c) xr[c] = act_value(act_dt, x, (int64_t)t * H + c);
+      if (w_dt == DT_MX4) {  // the token quantised to MXFP8, as the MX path multiplies it
+        std::vector<float> xf((size_t)H);
+        std::vector<uint8_t> codes((size_t)H), sc((size_t)H / 32);
+        for (int c = 0; c < H; ++c) xf[c] = (float)act_value(act_dt, x, (int64_t)t * H + c);
+        quant_mx8_row(H, xf.data(), codes.data(), sc.data(), xr.data());
+      } else {
+        for (int c = 0; c < H; ++c) xr[c] = act_value(act_dt, x, (int64_t)t * H + c);
+      }
       for (int i = 0; i < I; ++i) {
         double ag = 0.0, au = 0.0;
         const double* wg = &Wd[(size_t)i * H];
@@ -327,6 +408,15 @@ int oracle_down(int H, int I, int G, const int32_t* offsets, const double* h,
     parallel_for(r1 - r0, threads, [&](int64_t rr) {
       const int r = r0 + (int)rr;
       const double* hr = h + (int64_t)r * I;
+      std::vector<double> hq;
+      if (w_dt == DT_MX4) {  // h rounded to fp32, then quantised to MXFP8 per block of 32
+        std::vector<float> hf((size_t)I);
+        std::vector<uint8_t> codes((size_t)I), sc((size_t)I / 32);
+        hq.resize((size_t)I);
+        for (int i = 0; i < I; ++i) hf[i] = (float)hr[i];
+        quant_mx8_row(I, hf.data(), codes.data(), sc.data(), hq.data());
+        hr = hq.data();
+      }
       for (int n = 0; n < H; ++n) {
         double acc = 0.0;
         const double* wr = &Wd[(size_t)n * I];
@@ -363,6 +453,22 @@ void oracle_rmsnorm(int T, int H, double eps, const float* x, double* xn) {
     const double inv = 1.0 / std::sqrt(ss / H + eps);
     for (int h = 0; h < H; ++h) xn[(int64_t)t * H + h] = (double)x[(int64_t)t * H + h] * inv;
   }
+}
+
+// MXFP8 quantisation of rows [rows][cols] (cols % 32 == 0): codes [rows][cols],
+// scale bytes [rows][cols/32], and the values the codes stand for (fp64).
+void oracle_quant_mx8(int rows, int cols, const float* v, uint8_t* codes, uint8_t* scales, double* deq) {
+  for (int r = 0; r < rows; ++r)
+    quant_mx8_row(cols, v + (int64_t)r * cols, codes + (int64_t)r * cols, scales + (int64_t)r * (cols / 32),
+                  deq + (int64_t)r * cols);
+}
+
+// Decoded value of every MXFP4 weight of [G][N][K] (fp64).
+void oracle_mx4_values(int G, int N, int K, const uint8_t* w, const uint8_t* scales, double* out) {
+  const Weights W{DT_MX4, w, scales, nullptr, N, K};
+  for (int g = 0; g < G; ++g)
+    for (int n = 0; n < N; ++n)
+      for (int k = 0; k < K; ++k) out[((int64_t)g * N + n) * K + k] = W.value(g, n, k);
 }
 
 // Round fp64 values to bf16 (nearest, ties to even), returned as fp64.

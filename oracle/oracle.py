@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.cpp")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-DT = {"f32": 0, "bf16": 1, "i8": 2, "q4": 3}
+DT = {"f32": 0, "bf16": 1, "i8": 2, "q4": 3, "mx4": 4}
 
 
 def build(force: bool = True) -> str:
@@ -55,6 +55,10 @@ def lib():
         L.oracle_round_bf16.restype = None
         L.oracle_q4_values.argtypes = [i, i, i, p, p, p, p]
         L.oracle_q4_values.restype = None
+        L.oracle_quant_mx8.argtypes = [i, i, p, p, p, p]
+        L.oracle_quant_mx8.restype = None
+        L.oracle_mx4_values.argtypes = [i, i, i, p, p, p]
+        L.oracle_mx4_values.restype = None
         _lib = L
     return _lib
 
@@ -187,6 +191,25 @@ def q4_values(w, scale, mn) -> np.ndarray:
     out = np.empty((G, N, 2 * K2), np.float32)
     lib().oracle_q4_values(G, N, 2 * K2, _p(np.ascontiguousarray(w)), _p(np.ascontiguousarray(scale)),
                            _p(np.ascontiguousarray(mn)), _p(out))
+    return out
+
+
+def quant_mx8(v: np.ndarray):
+    """MXFP8 (E4M3, E8M0 scale per 32) of rows: -> (codes uint8 [rows][cols], scale bytes uint8
+    [rows][cols/32], values float64 [rows][cols])."""
+    v = np.ascontiguousarray(v, np.float32)
+    rows, cols = v.shape
+    codes = np.empty((rows, cols), np.uint8)
+    sc = np.empty((rows, cols // 32), np.uint8)
+    deq = np.empty((rows, cols), np.float64)
+    lib().oracle_quant_mx8(rows, cols, _p(v), _p(codes), _p(sc), _p(deq))
+    return codes, sc, deq
+
+
+def mx4_values(w, scales) -> np.ndarray:
+    G, N, K2 = w.shape
+    out = np.empty((G, N, 2 * K2), np.float64)
+    lib().oracle_mx4_values(G, N, 2 * K2, _p(np.ascontiguousarray(w)), _p(np.ascontiguousarray(scales)), _p(out))
     return out
 
 

@@ -490,3 +490,100 @@ def test_stack_composition_matches_dense():
     xn = bf16_rne_exact(x64 / np.sqrt((x64 ** 2).mean(1, keepdims=True) + eps))
     np.testing.assert_array_equal(bf16_f64(st["xn"]), xn)
     np.testing.assert_allclose(st["moe"] + x64, x1.astype(np.float64), rtol=0, atol=2e-6 * np.abs(x1).max())
+
+
+# ---- MX formats: MXFP4 weights, MXFP8 activations ---------------------------------
+
+def e4m3_grid():
+    """All finite E4M3 magnitudes with their codes, from the bit fields (exponent bias 7,
+    exponent 0 subnormal, the all-ones pattern reserved): an enumeration independent of
+    the oracle's rounding."""
+    mags, codes = [], []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        mags.append(m * 2.0 ** -9 if e == 0 else (8 + m) * 2.0 ** (e - 10))
+        codes.append(c)
+    return np.array(mags), np.array(codes)
+
+
+def test_mx_golden_blocks():
+    with open(os.path.join(GOLDEN, "mx_blocks.json")) as f:
+        fx = json.load(f)
+    m = fx["mxfp4"]
+    w = np.array(m["bytes"] * 2, np.uint8).reshape(1, 1, 32)
+    v = oracle.mx4_values(w, np.array(m["scales"], np.uint8).reshape(1, 1, 2))
+    np.testing.assert_array_equal(v[0, 0, :32], m["values_scale127"])
+    np.testing.assert_array_equal(v[0, 0, 32:], m["values_scale129"])
+    for b in fx["mxfp8"]:
+        c, s, d = oracle.quant_mx8(np.array([b["input"]], np.float32))
+        assert s[0, 0] == b["scale"]
+        np.testing.assert_array_equal(c[0], b["codes"])
+        np.testing.assert_array_equal(d[0], b["values"])
+
+
+def test_mx8_quant_is_nearest_e4m3_value():
+    """On random rows spanning many binades: each block's scale puts its largest
+    magnitude in [256, 512) (before saturation at 448), and every value becomes the
+    E4M3 value nearest to v / scale (ties to the even code), found by brute force over
+    the whole grid."""
+    rng = np.random.default_rng(5)
+    v = (rng.standard_normal((6, 256)) * 2.0 ** rng.integers(-30, 10, (6, 1))).astype(np.float32)
+    v[2, :32] = 0.0
+    codes, sc, deq = oracle.quant_mx8(v)
+    mags, gcodes = e4m3_grid()
+    for r in range(6):
+        for b in range(8):
+            blk = v[r, 32 * b:32 * b + 32].astype(np.float64)
+            s = int(sc[r, b])
+            if not blk.any():
+                assert s == 0 and not codes[r, 32 * b:32 * b + 32].any()
+                continue
+            X = 2.0 ** (s - 127)
+            assert 256 <= np.abs(blk).max() / X < 512
+            for j in range(32):
+                a = abs(blk[j]) / X
+                d = np.abs(mags - a)
+                best = np.flatnonzero(d == d.min())
+                want = gcodes[best[0]] if len(best) == 1 else [c for c in gcodes[best] if c % 2 == 0][0]
+                if a > 448:
+                    want = 126
+                if want == 0:
+                    assert codes[r, 32 * b + j] in (0, 0x80)
+                else:
+                    assert codes[r, 32 * b + j] == want | (0x80 if blk[j] < 0 else 0)
+                assert deq[r, 32 * b + j] == np.copysign(mags[want], blk[j]) * X
+
+
+def mx4_decode_np(w, s):
+    """MXFP4 values by table lookup (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; bit 3 the sign)."""
+    mag = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6] * 2) * np.repeat([1.0, -1.0], 8)
+    G, N, K2 = w.shape
+    c = np.empty((G, N, 2 * K2), np.int64)
+    c[..., 0::2] = w & 15
+    c[..., 1::2] = w >> 4
+    return mag[c] * np.repeat(2.0 ** (s.astype(np.float64) - 127), 32, axis=-1)
+
+
+@pytest.mark.parametrize("shape", [(64, 32, 4, 1, 0, 3), (128, 64, 16, 4, 1, 11), (256, 128, 32, 8, 1, 5)])
+def test_layer_mx4_matches_dense(shape):
+    """MXFP4 weights with MXFP8 activations: every token through every expert
+    (quantised token rows; h rounded to fp32 and quantised per block of 32 before
+    the down projection), dense gates, shared expert with weight 1."""
+    H, I, E, k, S, T = shape
+    d = make_case(H, I, E, k, S, T, "mx4", act="bf16", seed=41)
+    out = oracle.layer(d)
+    np.testing.assert_array_equal(oracle.mx4_values(d["w_gu"], d["w_gu_scale"]), mx4_decode_np(d["w_gu"], d["w_gu_scale"]))
+    wgu = mx4_decode_np(d["w_gu"], d["w_gu_scale"])
+    wdn = mx4_decode_np(d["w_down"], d["w_down_scale"])
+    x64 = x_f64(d)
+    _, ids, gates = np_route(x64, bf16_f64(d["w_router"]), k)
+    xq = oracle.quant_mx8(x64.astype(np.float32))[2]
+    dense = np.zeros((T, E))
+    for t in range(T):
+        dense[t, ids[t]] = gates[t]
+    ref = np.zeros((T, H))
+    for e in range(E + S):
+        hh = np_silu(xq @ wgu[e, :I].T) * (xq @ wgu[e, I:].T)
+        ye = oracle.quant_mx8(hh.astype(np.float32))[2] @ wdn[e].T
+        ref += ye if e == E else dense[:, e:e + 1] * ye
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
