@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_FP8_PEAK_TFLOPS = 5000.0   # dense fp8 (the rate of the FP4 x FP8 scaled MFMA, set by its FP8 operand)
 METRIC = "routed tokens/s per MoE layer (T=256 prefill, T=8 decode); % MFMA / HBM peak"
 
 
@@ -43,6 +44,8 @@ def weight_bytes(spec, n, k):
         return n * k * 2
     if spec.wt == "i8":
         return n * k + n * 4
+    if spec.wt == "mx4":
+        return n * k // 2 + n * k // 32
     return n * k // 2 + 2 * (n * k // 32) * 2
 
 
@@ -53,15 +56,21 @@ def act_bytes(spec):
 def gu_algorithmic_bytes(spec, T, U):
     """Gate/up launch: weights of the U touched groups, tokens read once, h written once."""
     R = T * (spec.top_k + spec.n_shared)
-    xb = T * spec.hidden * (1 if spec.wt == "i8" else act_bytes(spec)) + (T * 4 if spec.wt == "i8" else 0)
-    hb = R * spec.inter * (4 if spec.wt in ("f32", "i8") else 2)
+    if spec.wt == "mx4":
+        xb = T * spec.hidden + T * spec.hidden // 32  # E4M3 codes + E8M0 scales
+    else:
+        xb = T * spec.hidden * (1 if spec.wt == "i8" else act_bytes(spec)) + (T * 4 if spec.wt == "i8" else 0)
+    hb = R * spec.inter * (4 if spec.wt in ("f32", "i8", "mx4") else 2)
     return U * weight_bytes(spec, 2 * spec.inter, spec.hidden) + xb + hb
 
 
 def down_algorithmic_bytes(spec, T, U):
     R = T * (spec.top_k + spec.n_shared)
-    ib = R * spec.inter * (1 if spec.wt == "i8" else (4 if spec.wt == "f32" else 2))
-    yb = R * spec.hidden * (4 if spec.wt in ("f32", "i8") else 2)
+    if spec.wt == "mx4":
+        ib = R * spec.inter + R * spec.inter // 32
+    else:
+        ib = R * spec.inter * (1 if spec.wt == "i8" else (4 if spec.wt == "f32" else 2))
+    yb = R * spec.hidden * (4 if spec.wt in ("f32", "i8", "mx4") else 2)
     return U * weight_bytes(spec, spec.hidden, spec.inter) + ib + yb
 
 
@@ -319,6 +328,46 @@ def stack_figures():
     return out
 
 
+def mx4_figures(args):
+    """MXFP4 weights x MXFP8 activations: the T=2048 Zipf prefill (MFMA fraction
+    against the fp8 peak) and decode steps T = 1, 2, 4, 8 (HBM fraction of the
+    two GEMM launches, which read the touched groups' 4.25-bit weights)."""
+    import torch
+    out = {}
+    Tq = 2048
+    rq = Runner("mx4_e128_top8_shared_zipf", Tq, args.rotations, min(args.steps + args.warmup, 24))
+    stq = max(3, min(args.steps, 12))
+    wq, Uq, kq = rq.timed(stq, min(args.warmup, 3))
+    msq = wq / stq * 1e3
+    Rq = Tq * (rq.spec.top_k + rq.spec.n_shared)
+    fl_gu = 2.0 * Rq * 2 * rq.spec.inter * rq.spec.hidden
+    fl_dn = 2.0 * Rq * rq.spec.hidden * rq.spec.inter
+    out["prefill_mx4_zipf_t2048"] = {
+        "tokens_per_s": round(Tq / (msq / 1e3), 1), "ms_per_step": round(msq, 5),
+        "kernel_ms": {k: round(v, 5) for k, v in kq.items()}, "touched_groups": Uq,
+        "gate_up_mfma_frac_fp8": round(fl_gu / (kq["gate_up"] / 1e3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4),
+        "down_mfma_frac_fp8": round(fl_dn / (kq["down"] / 1e3) / 1e12 / MFMA_FP8_PEAK_TFLOPS, 4),
+    }
+    del rq
+    torch.cuda.empty_cache()
+    sweep = {}
+    for Td in (1, 2, 4, 8):
+        rd = Runner("mx4_e128_top8_shared", Td, args.rotations, args.steps + args.warmup)
+        wd, Ud, kd = rd.timed(args.steps, args.warmup)
+        msd = wd / args.steps * 1e3
+        b = gu_algorithmic_bytes(rd.spec, Td, Ud) + down_algorithmic_bytes(rd.spec, Td, Ud)
+        sweep[str(Td)] = {
+            "tokens_per_s": round(Td / (msd / 1e3), 1), "ms_per_step": round(msd, 5),
+            "kernel_ms": {k: round(v, 5) for k, v in kd.items()}, "touched_groups": Ud,
+            "gemm_hbm_frac": round(b / ((kd["gate_up"] + kd["down"]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemm_algorithmic_bytes": b,
+        }
+        del rd
+        torch.cuda.empty_cache()
+    out["decode_mx4_sweep"] = sweep
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,7 +380,7 @@ def main():
     ap.add_argument("--no-fp32", action="store_true", help="skip the fp32 16-expert figure")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer 4-bit stack figures")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
-    ap.add_argument("--workloads", default="headline,decode,fp32,q4,stack",
+    ap.add_argument("--workloads", default="headline,decode,fp32,q4,mx4,stack",
                     help="comma list of the parts to run (profiling runs pick one); without 'headline' the line's "
                          "value is null")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -451,6 +500,10 @@ def main():
                                     / MFMA_BF16_PEAK_TFLOPS, 4),
         }
         del rq
+        torch.cuda.empty_cache()
+
+    if "mx4" in parts:
+        extra.update(mx4_figures(args))
         torch.cuda.empty_cache()
 
     if not args.no_stack:

@@ -66,7 +66,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum moe_status {
   MOE_OK = 0,
@@ -80,7 +80,9 @@ typedef enum moe_dtype {
   MOE_F32 = 0,    /* IEEE binary32 */
   MOE_BF16 = 1,   /* bfloat16 bit patterns */
   MOE_I8 = 2,     /* int8 with one fp32 scale per output row (weights) or per token (activations) */
-  MOE_Q4B32 = 3   /* 4-bit unsigned codes in blocks of 32 along K, fp16 scale and fp16 min per block */
+  MOE_Q4B32 = 3,  /* 4-bit unsigned codes in blocks of 32 along K, fp16 scale and fp16 min per block */
+  MOE_MXFP4 = 4   /* OCP microscaling FP4: E2M1 elements in blocks of 32 along K, one E8M0 scale byte
+                     per block (weights only; the activations then go through MXFP8) */
 } moe_dtype;
 
 /* Shape and formats of one layer.  Supported combinations (act, w, out):
@@ -88,6 +90,10 @@ typedef enum moe_dtype {
  *   (BF16, BF16, BF16 or F32)
  *   (BF16, I8, BF16 or F32)    x quantised per token to int8 inside moe_permute
  *   (BF16, Q4B32, BF16 or F32) 4-bit weights dequantised to bf16 in registers
+ *   (BF16, MXFP4, BF16 or F32) x and h quantised to MXFP8 (E4M3 elements, one E8M0
+ *                              scale per 32) and multiplied by the scaled FP4 x FP8
+ *                              MFMA (the OCP MX formats; "MoE Decode Partition and
+ *                              Submit Floor", the FP4 data types it surveys)
  * Limits: hidden % 256 == 0, inter % 256 == 0, 1 <= n_routed <= 256,
  * 1 <= top_k <= min(16, n_routed), n_shared in {0, 1}, max_tokens >= 1 and
  * 6 * n_routed * ceil(max_tokens / 32) <= 61440 (the permutation keeps a token
@@ -114,6 +120,10 @@ typedef struct moe_desc {
  *             scale, min = fp16 bits [G][N][K/32];
  *             w_real = bf16_rne(fp32(scale * q + min)): scale * q is exact in fp32, the add
  *             rounds once to fp32, and that fp32 value is rounded once more to bf16. */
+/*   MXFP4:    w = uint8 [G][N][K/2] (byte b of a block: element 2b low nibble, 2b+1 high nibble,
+ *             each an E2M1 code: sign, 2 exponent bits with bias 1, 1 mantissa bit, so the
+ *             magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6); scale = uint8 E8M0 [G][N][K/32];
+ *             w_real = e2m1(code) * 2^(scale - 127) (exact); min = NULL. */
 typedef struct moe_weights {
   const void* w;
   const void* scale;
@@ -130,12 +140,12 @@ typedef struct moe_buffers {
   int32_t* row_token;       /* [R_max] token of each permuted row */
   int32_t* token_row;       /* [max_tokens][k+S] permuted row of each (token, slot); slot k = shared */
   int32_t* sched;           /* tile schedule: [0] = tile count, then {group, row0, rows, 0} per tile */
-  int8_t* x_q;              /* [max_tokens][H] int8 activations (I8 weights only, else may be NULL) */
-  float* x_scale;           /* [max_tokens] per-token activation scale (I8 only) */
-  void* h;                  /* [R_max][I] GLU output: F32 for F32/I8 weights, BF16 otherwise */
-  void* y;                  /* [R_max][H] down output per row: F32 for F32/I8 weights, BF16 otherwise */
-  int8_t* h_q;              /* [R_max][I] int8 GLU output, requantised per row (I8 only) */
-  float* h_scale;           /* [R_max] per-row scale of h_q (I8 only) */
+  int8_t* x_q;              /* [max_tokens][H] int8 activations (I8), E4M3 codes (MXFP4); else may be NULL */
+  float* x_scale;           /* I8: [max_tokens] per-token fp32 scale; MXFP4: uint8 E8M0 [max_tokens][H/32] */
+  void* h;                  /* [R_max][I] GLU output: F32 for F32/I8/MXFP4 weights, BF16 otherwise */
+  void* y;                  /* [R_max][H] down output per row: F32 for F32/I8/MXFP4 weights, BF16 otherwise */
+  int8_t* h_q;              /* [R_max][I] int8 (I8) or E4M3 (MXFP4) codes of h, quantised per row / block */
+  float* h_scale;           /* I8: [R_max] per-row fp32 scale; MXFP4: uint8 E8M0 [R_max][I/32] */
   uint32_t* sync;           /* 4096 bytes of grid-barrier words for moe_decode_layer: zero them once after
                                allocation; every completed call leaves them valid for the next one.
                                Word 640 is the status word: nonzero after a barrier wait timed out (then
@@ -168,8 +178,13 @@ moe_status moe_route_topk(const moe_desc* desc, int32_t T, const void* x, const 
  * expert_offsets, row_token, token_row and the tile schedule (tiles of at most
  * 64 rows of one group).  For I8 weights it also quantises x per token:
  * x_scale[t] = max_h |x[t][h]| / 127 and x_q = clamp(rne(x / x_scale), -127, 127)
- * (0 for an all-zero token).
- *   x: [T][H] act_dtype (read only for I8 weights; may be NULL otherwise)
+ * (0 for an all-zero token).  For MXFP4 weights it quantises x to MXFP8 in
+ * blocks of 32 along H (the OCP MX conversion): block max m = max |x|,
+ * x_scale byte = clamp(floor(log2 m) - 8 + 127, 0, 254) (8: the exponent of
+ * the largest E4M3 value, 448), x_q = the E4M3 code nearest x / 2^(byte - 127)
+ * (ties to even mantissa, magnitudes above 448 saturated to 448); an all-zero
+ * block has byte 0 and codes 0.
+ *   x: [T][H] act_dtype (read only for I8 and MXFP4 weights; may be NULL otherwise)
  * Reads bufs->topk_ids. */
 moe_status moe_permute(const moe_desc* desc, int32_t T, const void* x, const moe_buffers* bufs,
                        hipStream_t stream);
@@ -194,18 +209,23 @@ moe_status moe_route_permute(const moe_desc* desc, int32_t T, const void* x, con
  * Float weights: MFMA with fp32 accumulation, h stored in the h dtype.
  * I8 weights: exact int32 accumulation of x_q . w, then a = (fp32(acc) * x_scale[t]) * scale[g][n]
  * and h = (a_g / (1 + fp32(exp(-a_g)))) * a_u, each fp32 operation rounded once.
+ * MXFP4 weights: the scaled FP4 x FP8 MFMA of the weight blocks and the MXFP8 blocks of x_q
+ * (block scales applied inside the MFMA), fp32 accumulation, h in fp32.
  *   x: [T][H] act_dtype (unused for I8 weights, which read bufs->x_q / x_scale)
  * Reads expert_offsets, row_token, sched; writes bufs->h. */
 moe_status moe_grouped_gemm_gu(const moe_desc* desc, int32_t T, const void* x, const moe_weights* w_gu,
                                const moe_buffers* bufs, hipStream_t stream);
 
 /* Down projection of every permuted row, all groups in one launch (as for
- * gate/up; I8 weights add the per-row quantisation of h before it):
+ * gate/up; I8 and MXFP4 weights add one launch before it that quantises h):
  *   y[r][n] = h[r] . Wd[g][n].
  * I8 weights: each row of h is first quantised into h_q / h_scale
  * (s = max|h[r]| / 127, q = clamp(rne(h / s), -127, 127)); then
  * y = (fp32(acc) * s) * scale[g][n] with acc the exact int32 sum.
- * Reads h, expert_offsets, sched; writes bufs->y (and h_q, h_scale for I8). */
+ * MXFP4 weights: each row of h (fp32) is quantised to MXFP8 in blocks of 32
+ * (the conversion moe_permute applies to x) into h_q / h_scale; then the
+ * scaled FP4 x FP8 MFMA with fp32 accumulation gives y in fp32.
+ * Reads h, expert_offsets, sched; writes bufs->y (and h_q, h_scale for I8 and MXFP4). */
 moe_status moe_grouped_gemm_down(const moe_desc* desc, int32_t T, const moe_weights* w_down,
                                  const moe_buffers* bufs, hipStream_t stream);
 
@@ -238,7 +258,7 @@ moe_status moe_combine(const moe_desc* desc, int32_t T, const float* residual, v
  *   w_gu, w_down: as for the GEMM calls (BF16, I8 or Q4B32 weights)
  *   residual: [T][H] fp32 or NULL
  * Limits (else MOE_ERR_UNSUPPORTED): T * hidden <= 32768, inter <= 512,
- * hidden <= 8192, weights not F32. */
+ * hidden <= 8192, weights BF16, I8 or Q4B32. */
 #define MOE_DECODE_NORM_INPUT 1
 moe_status moe_decode_layer(const moe_desc* desc, int32_t T, const void* x, const void* w_router, const float* bias,
                             const moe_weights* w_gu, const moe_weights* w_down, const float* residual,

@@ -75,6 +75,34 @@ __device__ __forceinline__ u32x4 q4_decode8(uint32_t w, const Q4Block& b) {
   return f;
 }
 
+// MXFP8 block quantisation (OCP microscaling: 32 values share one E8M0 scale
+// byte, worth 2^(byte - 127); the elements are E4M3 -- bias 7, exponent 0
+// subnormal, largest 448).  Scale byte of a block with largest magnitude
+// amax: floor(log2(amax)) - 8 + 127 clamped to [0, 254] (8 = the exponent of
+// 448), or 0 for an all-zero block.
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+  if (!(amax > 0.f)) return 0u;
+  const int e = (int)((__float_as_uint(amax) >> 23) & 255u) - 127;  // amax is a normal fp32
+  return (uint32_t)min(254, max(0, e - 8 + 127));
+}
+// E4M3 code of v / 2^(byte - 127): the nearest E4M3 value (ties to the even
+// mantissa), magnitudes above 448 saturated to 448.  The quotient is exact (a
+// power-of-two scale); it is rounded to a multiple of 2^(max(E, -6) - 3), the
+// spacing of E4M3 values at its magnitude (E = its binary exponent).
+__device__ __forceinline__ uint32_t e4m3_code(float v, uint32_t byte) {
+  const float a = ldexpf(fabsf(v), 127 - (int)byte);
+  if (!(a > 0x1p-10f)) return 0u;  // at most half the smallest subnormal: rounds to 0
+  const int e = (int)((__float_as_uint(a) >> 23) & 255u) - 127;
+  const int qe = max(e, -6) - 3;
+  const float r = fminf(ldexpf(rintf(ldexpf(a, -qe)), qe), 448.f);
+  const int er = (int)((__float_as_uint(r) >> 23) & 255u) - 127;
+  uint32_t code;
+  if (r == 0.f) return 0u;
+  if (er >= -6) code = (uint32_t)((er + 7) << 3) | (uint32_t)(ldexpf(r, 3 - er) - 8.f);
+  else code = (uint32_t)ldexpf(r, 9);
+  return code | (v < 0.f ? 0x80u : 0u);
+}
+
 // Symmetric int8 code of v at scale s (s = max|row| / 127, IEEE division):
 // clamp(rne(v / s), -127, 127); s = 0 gives 0.  Returned as a float.
 __device__ __forceinline__ float quant_i8(float v, float s) {
@@ -94,6 +122,24 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ i32x4 mfma_i8_16x16x64(u32x4 a, u32x4 b, i32x4 c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, a), __builtin_bit_cast(i32x4, b), c, 0,
                                                 0, 0);
+}
+// v_mfma_scale_f32_16x16x128_f8f6f4 with A = FP4 (E2M1) and B = FP8 (E4M3),
+// D[i][j] += sum_k A[i][k] 2^(sa(i, k/32) - 127) B[k][j] 2^(sb(j, k/32) - 127).
+// Lane l supplies row / column l % 16.  A: lane group q = l / 16 holds K
+// 32q .. 32q+31 (16 bytes, element 2j in the low nibble of byte j); B: lane
+// group q holds K 16q .. 16q+15 (b0) and 64+16q .. 64+16q+15 (b1); each lane's
+// scale byte is that of K block q for its row / column.  The products are
+// exact; the MFMA adds them in groups of 8 consecutive K aligned to the
+// group's largest product, dropping bits below about 2^-14 of it, then adds
+// the group sums and C in fp32 (measured on gfx950), so a result is within
+// 2^-11 of the sum of |products| of the exact dot product.
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+__device__ __forceinline__ f32x4 mfma_mx4_mx8_16x16x128(u32x4 a, uint32_t sa, u32x4 b0, u32x4 b1, uint32_t sb,
+                                                        f32x4 c) {
+  const i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  const i32x8 bv = {(int)b0[0], (int)b0[1], (int)b0[2], (int)b0[3], (int)b1[0], (int)b1[1], (int)b1[2], (int)b1[3]};
+  // cbsz 4: A is FP4 (E2M1); blgp 0: B is FP8 (E4M3); scale bytes taken from byte 0
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, c, 4, 0, 0, (int)sa, 0, (int)sb);
 }
 __device__ __forceinline__ f32x4 mfma_f32_16x16x4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);

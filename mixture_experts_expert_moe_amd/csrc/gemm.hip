@@ -121,6 +121,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream) {
         case kBF16: return launch_fmt<kBF16, true, 4, 2>(a, stream);
         case kI8: return launch_fmt<kI8, true, 4, 2>(a, stream);
         case kQ4: return launch_fmt<kQ4, true, 4, 2>(a, stream);
+        case kMX4: return launch_fmt<kMX4, true, 4, 2>(a, stream);
         default: return hipErrorInvalidValue;
       }
     }
@@ -134,6 +135,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream) {
         if (a.T >= kQ4DownChunkMinT) return launch_fmt<kQ4, kGU, 2>(a, stream);
       }
       return launch_fmt<kQ4, kGU, 4>(a, stream);
+    case kMX4: return launch_fmt<kMX4, kGU, 2>(a, stream);  // 32-row items: no spills at two waves per SIMD
     default: return hipErrorInvalidValue;
   }
 }

@@ -33,6 +33,8 @@ template <>
 struct FmtTraits<kI8> { static constexpr int KS = 64; };
 template <>
 struct FmtTraits<kQ4> { static constexpr int KS = 128; };
+template <>
+struct FmtTraits<kMX4> { static constexpr int KS = 128; };  // one 16x16x128 scaled MFMA per stage
 
 // Stages per batch: a batch is what one wave keeps in flight while it computes
 // the previous one.  Fewer stages for tall tiles keeps the B registers bounded.
@@ -44,7 +46,7 @@ struct FmtTraits<kQ4> { static constexpr int KS = 128; };
 #endif
 template <int WF, int NSUB>
 constexpr int stages() {
-  return WF == kQ4 ? 1 : (NSUB <= 2 ? MOE_STAGES_SMALL : MOE_STAGES_LARGE);
+  return WF == kQ4 || WF == kMX4 ? 1 : (NSUB <= 2 ? MOE_STAGES_SMALL : MOE_STAGES_LARGE);
 }
 
 struct Kp {  // kernel parameters
@@ -77,6 +79,7 @@ __device__ __forceinline__ uint64_t ld_coh64(const void* p) {
 struct AStage {
   u32x4 v;               // raw 16 bytes
   Q4Block blk;           // 4-bit block parameters
+  uint32_t sc;           // MXFP4: the lane's E8M0 block scale byte
 };
 
 template <int WF>
@@ -87,6 +90,10 @@ __device__ __forceinline__ void load_a(AStage& s, const Kp& p, size_t wrow, int 
     s.v = ld16((const float*)p.w + wrow * p.K + k0 + 4 * q);
   } else if constexpr (WF == kI8) {
     s.v = ld16((const int8_t*)p.w + wrow * p.K + k0 + 16 * q);
+  } else if constexpr (WF == kMX4) {
+    // lane group q holds the whole 32-element block k0/32 + q and its scale
+    s.v = ld16((const uint8_t*)p.w + wrow * (size_t)(p.K / 2) + k0 / 2 + 16 * q);
+    s.sc = ((const uint8_t*)p.w_scale)[wrow * (size_t)(p.K / 32) + k0 / 32 + q];
   } else {
     // lane group q holds the whole 32-code block k0/32 + q
     s.v = ld16((const uint8_t*)p.w + wrow * (size_t)(p.K / 2) + k0 / 2 + 16 * q);
@@ -98,7 +105,8 @@ __device__ __forceinline__ void load_a(AStage& s, const Kp& p, size_t wrow, int 
 // Activation operand of one stage for one 16-row block (B operand).
 template <int WF>
 struct BStage {
-  u32x4 v[WF == kQ4 ? 4 : 1];
+  u32x4 v[WF == kQ4 ? 4 : WF == kMX4 ? 2 : 1];
+  uint32_t sc;  // MXFP8 activations: the lane's E8M0 block scale byte
 };
 
 template <int WF>
@@ -109,6 +117,14 @@ __device__ __forceinline__ void load_b(BStage<WF>& s, const Kp& p, size_t arow, 
     s.v[0] = ld16((const float*)p.act + arow * p.K + k0 + 4 * q);
   } else if constexpr (WF == kI8) {
     s.v[0] = ld16(p.act_q + arow * p.K + k0 + 16 * q);
+  } else if constexpr (WF == kMX4) {
+    // The FP8 operand of the 16x16x128 scaled MFMA: lane group q holds K
+    // k0+16q .. +15 in its first four registers and k0+64+16q .. +15 in the
+    // last four; its scale byte is that of block k0/32 + q, as for the FP4
+    // operand (whose lane group q holds the whole block).
+    s.v[0] = ld16(p.act_q + arow * p.K + k0 + 16 * q);
+    s.v[1] = ld16(p.act_q + arow * p.K + k0 + 64 + 16 * q);
+    s.sc = reinterpret_cast<const uint8_t*>(p.act_scale)[arow * (size_t)(p.K / 32) + k0 / 32 + q];
   } else {
 #pragma unroll
     for (int m = 0; m < 4; ++m) s.v[m] = ld16((const uint16_t*)p.act + arow * p.K + k0 + 32 * q + 8 * m);
@@ -141,6 +157,8 @@ __device__ __forceinline__ void mma_stage(Acc<WF> (&acc)[NA][NSUB], const AStage
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             acc[n][s] = mfma_f32_16x16x4(__uint_as_float(a[n].v[j]), __uint_as_float(b[s].v[0][j]), acc[n][s]);
+        } else if constexpr (WF == kMX4) {
+          acc[n][s] = mfma_mx4_mx8_16x16x128(a[n].v, a[n].sc, b[s].v[0], b[s].v[1], b[s].sc, acc[n][s]);
         } else {
           acc[n][s] = mfma_i8_16x16x64(a[n].v, b[s].v[0], acc[n][s]);
         }
@@ -198,7 +216,7 @@ __device__ __forceinline__ void store_gu(const Kp& p, int r, int col, const Acc<
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = silu_fast(g[i]) * u[i];
   }
-  store4<kCoh>(p, WF == kF32 || WF == kI8, r, col, v);
+  store4<kCoh>(p, WF == kF32 || WF == kI8 || WF == kMX4, r, col, v);
 }
 
 template <int WF, bool kCoh>
@@ -213,7 +231,7 @@ __device__ __forceinline__ void store_down(const Kp& p, int r, int col, const Ac
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[i] = y[i];
   }
-  store4<kCoh>(p, WF == kF32 || WF == kI8, r, col, v);
+  store4<kCoh>(p, WF == kF32 || WF == kI8 || WF == kMX4, r, col, v);
 }
 
 // 16-row weight blocks per work item: 4 (gate/up: 32 gate/up pairs; down: 64

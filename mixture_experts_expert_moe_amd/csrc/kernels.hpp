@@ -7,7 +7,7 @@
 
 namespace moe {
 
-enum WFmt { kF32 = 0, kBF16 = 1, kI8 = 2, kQ4 = 3 };
+enum WFmt { kF32 = 0, kBF16 = 1, kI8 = 2, kQ4 = 3, kMX4 = 4 };
 
 struct RouteArgs {
   const void* x;
@@ -103,6 +103,10 @@ inline size_t route_partials_bytes(int64_t max_tokens, int64_t E) {
 inline size_t route_partials_offset(int64_t max_tokens, int64_t E) { return ((size_t)max_tokens * E * 4 + 15) / 16 * 16; }
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream);
 hipError_t launch_quant_rows(const QuantArgs& a, hipStream_t stream);
+// MXFP8 (E4M3 codes, one E8M0 scale byte per 32 values) of rows of bf16 or
+// fp32 values; cols % 256 == 0.
+hipError_t launch_quant_mx8_rows(const void* src, bool src_f32, uint8_t* codes, uint8_t* scales, int64_t rows,
+                                 int cols, hipStream_t stream);
 hipError_t launch_gate_up(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_down(const GemmArgs& a, hipStream_t stream);
 // Register-A / LDS-B grouped GEMMs over the big tiles (bf16 or 4-bit) and,

@@ -16,6 +16,10 @@ using moe::kF32;
 using moe::kI8;
 using moe::kQ4;
 
+// Weights whose activations are quantised before the GEMMs (x_q, h_q).
+bool quant_act(const moe_desc* d) { return d->w_dtype == MOE_I8 || d->w_dtype == MOE_MXFP4; }
+bool mx(const moe_desc* d) { return d->w_dtype == MOE_MXFP4; }
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 moe_status check_desc(const moe_desc* d) {
@@ -27,7 +31,7 @@ moe_status check_desc(const moe_desc* d) {
   if (d->n_routed > 256 || d->top_k > 16) return MOE_ERR_UNSUPPORTED;
   if (moe::permute_lds_bytes(d->max_tokens, d->n_routed) > moe::kPermuteMaxLds) return MOE_ERR_UNSUPPORTED;
   const int a = d->act_dtype, w = d->w_dtype, o = d->out_dtype;
-  if (a < MOE_F32 || a > MOE_Q4B32 || w < MOE_F32 || w > MOE_Q4B32 || o < MOE_F32 || o > MOE_Q4B32)
+  if (a < MOE_F32 || a > MOE_MXFP4 || w < MOE_F32 || w > MOE_MXFP4 || o < MOE_F32 || o > MOE_MXFP4)
     return MOE_ERR_INVALID_ARG;
   if (o != MOE_F32 && o != MOE_BF16) return MOE_ERR_UNSUPPORTED;
   if (a == MOE_F32) {
@@ -53,7 +57,9 @@ bool ptr_ok(const void* p) { return p && aligned16(p); }
 
 int groups(const moe_desc* d) { return d->n_routed + d->n_shared; }
 int64_t rows(const moe_desc* d, int64_t T) { return T * (d->top_k + d->n_shared); }
-bool f32_intermediates(const moe_desc* d) { return d->w_dtype == MOE_F32 || d->w_dtype == MOE_I8; }
+bool f32_intermediates(const moe_desc* d) {
+  return d->w_dtype == MOE_F32 || d->w_dtype == MOE_I8 || d->w_dtype == MOE_MXFP4;
+}
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -81,6 +87,7 @@ moe_status check_weights(const moe_desc* d, const moe_weights* w) {
   if (!w || !ptr_ok(w->w)) return MOE_ERR_INVALID_ARG;
   if (d->w_dtype == MOE_I8 && !ptr_ok(w->scale)) return MOE_ERR_INVALID_ARG;
   if (d->w_dtype == MOE_Q4B32 && (!ptr_ok(w->scale) || !ptr_ok(w->min))) return MOE_ERR_INVALID_ARG;
+  if (d->w_dtype == MOE_MXFP4 && !ptr_ok(w->scale)) return MOE_ERR_INVALID_ARG;
   return MOE_OK;
 }
 
@@ -108,7 +115,7 @@ moe_status moe_buffer_sizes(const moe_desc* d, size_t sizes[MOE_NUM_BUFFERS]) {
   const size_t M = (size_t)d->max_tokens, E = (size_t)d->n_routed, k = (size_t)d->top_k;
   const size_t S = (size_t)d->n_shared, H = (size_t)d->hidden, I = (size_t)d->inter;
   const size_t G = E + S, Rmax = M * (k + S);
-  const bool i8 = d->w_dtype == MOE_I8;
+  const bool i8 = d->w_dtype == MOE_I8, q = quant_act(d), m = mx(d);
   const size_t fw = f32_intermediates(d) ? 4 : 2;
   sizes[0] = moe::route_partials_offset(M, E) + moe::route_partials_bytes(M, E);  // logits + fused-route scratch
   sizes[1] = M * k * 4;                                  // topk_ids
@@ -117,12 +124,12 @@ moe_status moe_buffer_sizes(const moe_desc* d, size_t sizes[MOE_NUM_BUFFERS]) {
   sizes[4] = Rmax * 4;                                   // row_token
   sizes[5] = M * (k + S) * 4;                            // token_row
   sizes[6] = moe::sched_ints((int64_t)Rmax, (int64_t)G) * 4;  // sched
-  sizes[7] = i8 ? M * H : 0;                             // x_q
-  sizes[8] = i8 ? M * 4 : 0;                             // x_scale
+  sizes[7] = q ? M * H : 0;                              // x_q
+  sizes[8] = i8 ? M * 4 : m ? M * (H / 32) : 0;          // x_scale
   sizes[9] = Rmax * I * fw;                              // h
   sizes[10] = Rmax * H * fw;                             // y
-  sizes[11] = i8 ? Rmax * I : 0;                         // h_q
-  sizes[12] = i8 ? Rmax * 4 : 0;                         // h_scale
+  sizes[11] = q ? Rmax * I : 0;                          // h_q
+  sizes[12] = i8 ? Rmax * 4 : m ? Rmax * (I / 32) : 0;   // h_scale
   sizes[13] = moe::kDecodeSyncBytes;                     // sync
   return MOE_OK;
 }
@@ -151,11 +158,16 @@ moe_status moe_permute(const moe_desc* d, int32_t T, const void* x, const moe_bu
       !ptr_ok(b->sched))
     return MOE_ERR_INVALID_ARG;
   const bool i8 = d->w_dtype == MOE_I8;
-  if (i8 && (!ptr_ok(x) || !ptr_ok(b->x_q) || !ptr_ok(b->x_scale))) return MOE_ERR_INVALID_ARG;
+  if (quant_act(d) && (!ptr_ok(x) || !ptr_ok(b->x_q) || !ptr_ok(b->x_scale))) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (i8) {
     moe::QuantArgs q{x, d->act_dtype == MOE_F32, b->x_q, b->x_scale, nullptr, T, d->hidden};
     const hipError_t e = moe::launch_quant_rows(q, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (mx(d)) {
+    const hipError_t e = moe::launch_quant_mx8_rows(x, d->act_dtype == MOE_F32, (uint8_t*)b->x_q,
+                                                    (uint8_t*)b->x_scale, T, d->hidden, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
@@ -173,7 +185,7 @@ moe_status moe_route_permute(const moe_desc* d, int32_t T, const void* x, const 
   if (!ptr_ok(b->logits) || !ptr_ok(b->topk_ids) || !ptr_ok(b->topk_w) || !ptr_ok(b->expert_offsets) ||
       !ptr_ok(b->row_token) || !ptr_ok(b->token_row) || !ptr_ok(b->sched))
     return MOE_ERR_INVALID_ARG;
-  if (i8 && (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale))) return MOE_ERR_INVALID_ARG;
+  if (quant_act(d) && (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale))) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   if (T > moe::kSmallRouteT) {
     if ((s = moe_route_topk(d, T, x, w_router, bias, b, stream)) != MOE_OK) return s;
@@ -191,6 +203,11 @@ moe_status moe_route_permute(const moe_desc* d, int32_t T, const void* x, const 
   a.slices = slices;
   a.x_q = i8 ? b->x_q : nullptr;
   a.x_scale = i8 ? b->x_scale : nullptr;
+  if (mx(d)) {
+    const hipError_t e = moe::launch_quant_mx8_rows(x, d->act_dtype == MOE_F32, (uint8_t*)b->x_q,
+                                                    (uint8_t*)b->x_scale, T, d->hidden, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
   return hip_status(moe::launch_route_permute_small(a, stream));
 }
 
@@ -199,14 +216,14 @@ moe_status moe_grouped_gemm_gu(const moe_desc* d, int32_t T, const void* x, cons
   moe_status s = check_call(d, T, b);
   if (s != MOE_OK) return s;
   if ((s = check_weights(d, w)) != MOE_OK) return s;
-  const bool i8 = d->w_dtype == MOE_I8;
-  if (i8 ? (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale)) : !ptr_ok(x)) return MOE_ERR_INVALID_ARG;
+  const bool q = quant_act(d);
+  if (q ? (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale)) : !ptr_ok(x)) return MOE_ERR_INVALID_ARG;
   if (!ptr_ok(b->row_token) || !ptr_ok(b->sched) || !ptr_ok(b->h)) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   moe::GemmArgs a{};
-  a.act = i8 ? nullptr : x;
-  a.act_q = i8 ? b->x_q : nullptr;
-  a.act_scale = i8 ? b->x_scale : nullptr;
+  a.act = q ? nullptr : x;
+  a.act_q = q ? b->x_q : nullptr;
+  a.act_scale = q ? b->x_scale : nullptr;
   a.row_token = b->row_token;
   a.sched = b->sched;
   a.w = w->w;
@@ -233,20 +250,25 @@ moe_status moe_grouped_gemm_down(const moe_desc* d, int32_t T, const moe_weights
   moe_status s = check_call(d, T, b);
   if (s != MOE_OK) return s;
   if ((s = check_weights(d, w)) != MOE_OK) return s;
-  const bool i8 = d->w_dtype == MOE_I8;
+  const bool i8 = d->w_dtype == MOE_I8, q = quant_act(d);
   if (!ptr_ok(b->h) || !ptr_ok(b->sched) || !ptr_ok(b->y)) return MOE_ERR_INVALID_ARG;
-  if (i8 && (!ptr_ok(b->h_q) || !ptr_ok(b->h_scale))) return MOE_ERR_INVALID_ARG;
+  if (q && (!ptr_ok(b->h_q) || !ptr_ok(b->h_scale))) return MOE_ERR_INVALID_ARG;
   if (T == 0) return MOE_OK;
   const int R = (int)rows(d, T);
   if (i8) {
-    moe::QuantArgs q{b->h, true, b->h_q, b->h_scale, nullptr, R, d->inter};
-    const hipError_t e = moe::launch_quant_rows(q, stream);
+    moe::QuantArgs qa{b->h, true, b->h_q, b->h_scale, nullptr, R, d->inter};
+    const hipError_t e = moe::launch_quant_rows(qa, stream);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+  }
+  if (mx(d)) {
+    const hipError_t e =
+        moe::launch_quant_mx8_rows(b->h, true, (uint8_t*)b->h_q, (uint8_t*)b->h_scale, R, d->inter, stream);
     if (e != hipSuccess) return MOE_ERR_HIP;
   }
   moe::GemmArgs a{};
-  a.act = i8 ? nullptr : b->h;
-  a.act_q = i8 ? b->h_q : nullptr;
-  a.act_scale = i8 ? b->h_scale : nullptr;
+  a.act = q ? nullptr : b->h;
+  a.act_q = q ? b->h_q : nullptr;
+  a.act_scale = q ? b->h_scale : nullptr;
   a.row_token = nullptr;
   a.sched = b->sched;
   a.w = w->w;
@@ -313,7 +335,8 @@ moe_status moe_decode_layer(const moe_desc* d, int32_t T, const void* x, const v
     return MOE_ERR_INVALID_ARG;
   if (i8 && (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale) || !ptr_ok(b->h_q) || !ptr_ok(b->h_scale)))
     return MOE_ERR_INVALID_ARG;
-  if (d->act_dtype != MOE_BF16 || d->w_dtype == MOE_F32 || (norm && d->out_dtype != MOE_F32))
+  if (d->act_dtype != MOE_BF16 || d->w_dtype == MOE_F32 || d->w_dtype == MOE_MXFP4 ||
+      (norm && d->out_dtype != MOE_F32))
     return MOE_ERR_UNSUPPORTED;
   if (T > moe::kDecodeMaxT || (int64_t)T * d->hidden > moe::kDecodeMaxTH || d->inter > moe::kDecodeMaxI ||
       d->hidden > 8192)

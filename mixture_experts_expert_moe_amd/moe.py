@@ -13,8 +13,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libmoe_gfx950.so")
 
-MOE_F32, MOE_BF16, MOE_I8, MOE_Q4B32 = 0, 1, 2, 3
-DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8, "q4": MOE_Q4B32}
+MOE_F32, MOE_BF16, MOE_I8, MOE_Q4B32, MOE_MXFP4 = 0, 1, 2, 3, 4
+DTYPE_CODE = {"f32": MOE_F32, "bf16": MOE_BF16, "i8": MOE_I8, "q4": MOE_Q4B32, "mx4": MOE_MXFP4}
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3: "MOE_ERR_BUFFER_TOO_SMALL",
           -4: "MOE_ERR_HIP"}
 

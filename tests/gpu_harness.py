@@ -9,6 +9,14 @@ from gen.synth import LayerSpec
 
 TOL_BF16 = dict(max_rel=2e-2, rmse=5e-3)   # bf16 / 4-bit outputs vs the fp64 oracle
 TOL_F32 = dict(max_rel=1e-4, rmse=2e-6)    # fp32 path (MFMA fp32 accumulation over K <= 2048)
+# The scaled FP4 x FP8 MFMA forms exact products, adds them in groups of 8
+# consecutive K aligned to the group's largest product with the bits below
+# about 2^-14 of it dropped (measured on gfx950: an addend under that
+# threshold next to a large product vanishes, the same addend alone is kept),
+# then adds the group sums in fp32.  Seven dropped remainders per group stay
+# under 2^-11 of the group's largest |product|, so a dot product is within
+# MX_ACC * sum_k |a_k w_k| of the exact one.
+MX_ACC = 2.0 ** -11
 
 
 def torch_mod():
@@ -85,12 +93,62 @@ def assert_close(got, ref, max_rel, rmse, what=""):
     return mr, rm
 
 
+def assert_within(got, ref, bound, what=""):
+    """|got - ref| <= bound element by element."""
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), "%s: non-finite values" % what
+    err = np.abs(got - ref)
+    bad = err > bound
+    if bad.any():
+        i = np.unravel_index(np.argmax(err / np.maximum(bound, 1e-300)), err.shape)
+        raise AssertionError("%s: %d of %d elements beyond the bound; worst at %s: got %.9g ref %.9g bound %.3g"
+                             % (what, int(bad.sum()), bad.size, i, got[i], ref[i], bound[i]))
+    return float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+
+
+def mx_gu_bound(d: dict, offsets, row_token) -> np.ndarray:
+    """Bound on |h_gpu - h_oracle| for MXFP4 gate/up: the MFMA bound on g and u
+    (MX_ACC * sum |products|) carried through h = silu(g) u (|silu'| <= 1.1),
+    plus 1e-6 |h| for the fp32 rounding and the fast exp of SiLU."""
+    from oracle import oracle
+    I = d["spec"].inter
+    xq = oracle.quant_mx8(bf16_to_f64(d["x"]).astype(np.float32))[2]
+    W = oracle.mx4_values(d["w_gu"], d["w_gu_scale"])
+    bound = np.zeros((int(offsets[-1]), I))
+    for g in range(len(offsets) - 1):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 == r0:
+            continue
+        a = xq[row_token[r0:r1]]
+        gu = a @ W[g].T
+        s = np.abs(a) @ np.abs(W[g]).T
+        gg, uu = gu[:, :I], gu[:, I:]
+        dg, du = MX_ACC * s[:, :I], MX_ACC * s[:, I:]
+        silu = gg / (1.0 + np.exp(-gg))
+        bound[r0:r1] = 1.1 * dg * (np.abs(uu) + du) + np.abs(silu) * du + 1e-6 * np.abs(silu * uu)
+    return bound
+
+
+def mx_down_bound(d: dict, offsets, h_in: np.ndarray, y_ref: np.ndarray) -> np.ndarray:
+    """Bound on |y_gpu - y_oracle| for MXFP4 down fed the fp32 rows h_in (both
+    sides quantise them to the same MXFP8 codes)."""
+    from oracle import oracle
+    hq = oracle.quant_mx8(np.asarray(h_in, np.float32))[2]
+    W = oracle.mx4_values(d["w_down"], d["w_down_scale"])
+    bound = np.zeros_like(y_ref)
+    for g in range(len(offsets) - 1):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 > r0:
+            bound[r0:r1] = MX_ACC * (np.abs(hq[r0:r1]) @ np.abs(W[g]).T)
+    return bound + 1e-6 * np.abs(y_ref)
+
+
 def tol_for(spec: LayerSpec):
     return TOL_F32 if spec.wt == "f32" else TOL_BF16
 
 
 def h_dtype(spec):
-    return np.float32 if spec.wt in ("f32", "i8") else np.uint16
+    return np.float32 if spec.wt in ("f32", "i8", "mx4") else np.uint16
 
 
 def decode(arr, dt):

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_function():
     L = moe.lib()
     for n in names:
         assert hasattr(L, n), n
-    assert L.moe_abi_version() == 3
+    assert L.moe_abi_version() == 4
 
 
 def test_status_strings():
@@ -66,6 +66,11 @@ def test_buffer_sizes_match_shapes():
     s8 = moe.moe_buffer_sizes(desc(wt="i8"))
     assert s8["x_q"] == 256 * 2048 and s8["h_q"] == R * 512 and s8["h"] == R * 512 * 4
     assert s["sync"] == s8["sync"] == 4096
+    # MXFP4 weights: E4M3 codes of x and h, one E8M0 byte per 32 values, fp32 h and y
+    sm = moe.moe_buffer_sizes(desc(wt="mx4"))
+    assert sm["x_q"] == 256 * 2048 and sm["x_scale"] == 256 * 2048 // 32
+    assert sm["h_q"] == R * 512 and sm["h_scale"] == R * 512 // 32
+    assert sm["h"] == R * 512 * 4 and sm["y"] == R * 2048 * 4
 
 
 @pytest.mark.parametrize("kw,code", [

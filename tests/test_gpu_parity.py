@@ -57,6 +57,13 @@ SMALL = [
     ("q4_e8k2s1_t1100_big", 256, 256, 8, 2, 1, 1100, "q4", 0.0),
     ("q4_e16k4s1_t1024_zipf_big", 256, 512, 16, 4, 1, 1024, "q4", 1.1),
     ("q4_e256k16_t1100_zipf_big", 256, 256, 256, 16, 0, 1100, "q4", 1.1),
+    # MXFP4 weights x MXFP8 activations (scaled FP4 x FP8 MFMA): 16-pair gate/up
+    # items (T <= 16, few-token routing), 32-row items with ragged tails, a
+    # Zipf-skewed routing, and T >= 1024 (no big tiles for this format)
+    ("mx4_e32k8s1_t9", 512, 512, 32, 8, 1, 9, "mx4", 0.0),
+    ("mx4_e16k4s1_t37", 256, 256, 16, 4, 1, 37, "mx4", 0.0),
+    ("mx4_e16k2s1_t200_zipf", 512, 256, 16, 2, 1, 200, "mx4", 1.1),
+    ("mx4_e8k2s1_t1100", 256, 256, 8, 2, 1, 1100, "mx4", 0.0),
 ]
 
 
@@ -108,6 +115,13 @@ def run_steps(name, d):
         np.testing.assert_array_equal(gh.buf(g.layer, "x_scale", np.float32, (T,)), xs)
         h_ref = oracle.gate_up(None, offsets, row_token, spec.inter, "i8", d["w_gu"], d["w_gu_scale"], xq=xq, xs=xs)
         np.testing.assert_array_equal(g.h_raw(), h_ref.astype(np.float32), err_msg="int8 gate/up (exact fp32)")
+    elif spec.wt == "mx4":
+        xc, xsc, _ = oracle.quant_mx8(gh.bf16_to_f64(d["x"]).astype(np.float32))
+        np.testing.assert_array_equal(gh.buf(g.layer, "x_q", np.uint8, (T, spec.hidden)), xc, err_msg="x E4M3 codes")
+        np.testing.assert_array_equal(gh.buf(g.layer, "x_scale", np.uint8, (T, spec.hidden // 32)), xsc,
+                                      err_msg="x E8M0 scales")
+        h_ref = oracle.gate_up(d["x"], offsets, row_token, spec.inter, "mx4", d["w_gu"], d["w_gu_scale"])
+        gh.assert_within(g.h(), h_ref, gh.mx_gu_bound(d, offsets, row_token), what="MX gate/up h")
     else:
         h_ref = oracle.gate_up(d["x"], offsets, row_token, spec.inter, spec.wt, d["w_gu"], d["w_gu_scale"],
                                d["w_gu_min"])
@@ -128,6 +142,13 @@ def run_steps(name, d):
         np.testing.assert_array_equal(gh.buf(g.layer, "h_q", np.int8, (R, spec.inter)), hq_ref, err_msg="h_q")
         np.testing.assert_array_equal(gh.buf(g.layer, "h_scale", np.float32, (R,)), hs_ref, err_msg="h_scale")
         np.testing.assert_array_equal(g.y_raw(), y_ref.astype(np.float32), err_msg="int8 down (exact)")
+    elif spec.wt == "mx4":
+        hc, hsc, _ = oracle.quant_mx8(h_ref.astype(np.float32))
+        R = h_ref.shape[0]
+        np.testing.assert_array_equal(gh.buf(g.layer, "h_q", np.uint8, (R, spec.inter)), hc, err_msg="h E4M3 codes")
+        np.testing.assert_array_equal(gh.buf(g.layer, "h_scale", np.uint8, (R, spec.inter // 32)), hsc,
+                                      err_msg="h E8M0 scales")
+        gh.assert_within(g.y(), y_ref, gh.mx_down_bound(d, offsets, h_in, y_ref), what="MX down y")
     else:
         gh.assert_close(g.y(), y_ref, what="down y", **tol)
     # combine, fed the oracle's y in the GPU's y format
@@ -263,6 +284,7 @@ FUSED_ROUTE = [
     ("q4_e16k4s1_t4_zipf", 512, 256, 16, 4, 1, 4, "q4", 1.1),
     ("bf16_e8k8s1_t3_h256", 256, 256, 8, 8, 1, 3, "bf16", 0.0),
     ("bf16_e256k16_t16", 1024, 256, 256, 16, 0, 16, "bf16", 0.0),
+    ("mx4_e128k8s1_t5", 2048, 512, 128, 8, 1, 5, "mx4", 0.0),
 ]
 
 ROUTE_PERMUTE_BUFFERS = ("topk_ids", "topk_w", "expert_offsets", "row_token", "token_row", "sched", "x_q", "x_scale")
@@ -290,7 +312,7 @@ def test_route_permute_matches_separate_calls(case):
     check_permute(g, oracle.permute(ref_route[1], spec.n_routed, spec.n_shared))
     # every other buffer the two calls write, bit for bit (only the bytes the calls define)
     nbytes = dict(topk_ids=T * k * 4, topk_w=T * k * 4, expert_offsets=(E + S + 1) * 4, row_token=T * (k + S) * 4,
-                  token_row=T * (k + S) * 4, x_q=T * H, x_scale=T * 4)
+                  token_row=T * (k + S) * 4, x_q=T * H, x_scale=T * (H // 32 if wt == "mx4" else 4))
     head, small, big = g.sched()
     nbytes["sched"] = (32 + 4 * len(small)) * 4
     for n, t in ref.items():
@@ -301,6 +323,10 @@ def test_route_permute_matches_separate_calls(case):
         xq, xs = oracle.quantize_x(spec, d["x"])
         np.testing.assert_array_equal(gh.buf(g.layer, "x_q", np.int8, (T, H)), xq)
         np.testing.assert_array_equal(gh.buf(g.layer, "x_scale", np.float32, (T,)), xs)
+    if wt == "mx4":
+        xc, xsc, _ = oracle.quant_mx8(gh.bf16_to_f64(d["x"]).astype(np.float32))
+        np.testing.assert_array_equal(gh.buf(g.layer, "x_q", np.uint8, (T, H)), xc)
+        np.testing.assert_array_equal(gh.buf(g.layer, "x_scale", np.uint8, (T, H // 32)), xsc)
 
 
 # Planted ties: router rows 5 and 9 copy row 2, so those three experts get
@@ -331,3 +357,28 @@ def test_route_ties_and_zero_token(T, fused):
     for t in range(T):
         tied = [e for e in ids[t] if e in (2, 5, 9)]
         assert tied == sorted(tied), (t, ids[t])
+
+
+def test_layer_mx4_zipf_prefill_full():
+    """MXFP4 weights x MXFP8 activations at T = 2048 with Zipf-skewed routing,
+    every token: the x and h codes bit for bit, every h and y row, then the
+    whole layer end to end."""
+    d = synth.layer_inputs("mx4_e128_top8_shared_zipf", 2048)
+    say("layer mx4_e128_top8_shared_zipf T=2048 (steps)")
+    run_steps("mx4_e128_top8_shared_zipf", d)
+    say("layer mx4_e128_top8_shared_zipf T=2048 (end to end)")
+    g2 = gh.GpuLayer(d)
+    g2.run()
+    mr, rm = gh.assert_close(g2.output(), oracle.layer(d), what="mx4 layer (all 2048 tokens)", **gh.TOL_BF16)
+    say("mx4 T=2048: max_rel %.3g rmse %.3g" % (mr, rm))
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_layer_mx4_decode_full(T):
+    d = synth.layer_inputs("mx4_e128_top8_shared", T, stream=T)
+    say("layer mx4_e128_top8_shared T=%d" % T)
+    run_steps("mx4_e128_top8_shared", d)
+    g2 = gh.GpuLayer(d)
+    g2.run()
+    mr, rm = gh.assert_close(g2.output(), oracle.layer(d), what="mx4 layer", **gh.TOL_BF16)
+    say("mx4 T=%d: max_rel %.3g rmse %.3g" % (T, mr, rm))
