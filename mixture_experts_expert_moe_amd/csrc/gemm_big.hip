@@ -28,6 +28,12 @@
 // lane's 16-byte load is one whole 32-code block (one scale, one min); the
 // token fragments are read from LDS in the same order, which leaves the dot
 // products unchanged.
+// MXFP4 weights (E2M1, one E8M0 scale per 32) against MXFP8 token rows take
+// the same loop with one scaled FP4 x FP8 MFMA (16x16x128) per fragment pair
+// and super-stage: a lane's 16-byte weight load is its whole 32-element block
+// plus one scale byte, nothing is decoded, the token rows are 128 bytes per
+// super-stage in LDS, and their scale bytes (4 per row) are copied into LDS
+// next to them by the same DMA.
 //
 // The shared expert and every routed expert go through the same launch; the
 // grouping itself is the point of the pages' "concatenated-expert" fix
@@ -57,20 +63,39 @@ constexpr int ring() { return WF == kQ4 ? MOE_BIG_RING_Q4 : 3; }
 static_assert(MOE_BIG_RING_Q4 == 2 || MOE_BIG_RING_Q4 == 3, "ring depth");
 constexpr int kThreads = 256;
 // Token rows per block: kBigTileRows for the big-tile list, kTileRows for the
-// small-tile list.  B stage bytes, and DMA instructions per wave per stage
-// (each covers 4 rows of 256 bytes).
-template <int BM> constexpr int b_stage_bytes() { return BM * kSK * 2; }
-template <int BM> constexpr int b_dma_per_wave() { return BM / 16; }
+// small-tile list.  Bytes of one token row per super-stage (bf16: 256, E4M3:
+// 128), 16-byte chunks per row, rows per 1 KB DMA instruction; B stage bytes
+// (MX: the rows, then 4 scale bytes per row), and DMA instructions per wave
+// per stage for the rows.
+template <int WF> constexpr int b_row_bytes() { return WF == kMX4 ? kSK : kSK * 2; }
+template <int WF> constexpr int b_row_chunks() { return b_row_bytes<WF>() / 16; }
+template <int WF> constexpr int b_rows_per_dma() { return 1024 / b_row_bytes<WF>(); }
+template <int WF, int BM> constexpr int b_data_bytes() { return BM * b_row_bytes<WF>(); }
+// MX scale area: each wave's DMA writes 64 dwords (256 bytes); lane l of wave
+// w holds the 4 scale bytes of token row BM / 4 * w + l % (BM / 4) (lanes
+// past BM / 4 repeat rows, so that every lane of the DMA is active).
+template <int WF, int BM> constexpr int b_stage_bytes() { return b_data_bytes<WF, BM>() + (WF == kMX4 ? 1024 : 0); }
+template <int BM> __device__ __forceinline__ constexpr int b_scale_off(int row) {
+  return 256 * (row / (BM / 4)) + 4 * (row % (BM / 4));
+}
+template <int WF, int BM> constexpr int b_dma_per_wave() { return b_data_bytes<WF, BM>() / 1024 / 4; }
+// Chunk slot of a row's 16-byte chunk c in LDS: XOR-swizzled by row so that
+// the 16 rows of a fragment read spread over the banks (256-byte rows: all
+// 16 slots; 128-byte rows: two rows per 256 bytes, 8 slots each).
+template <int WF> __device__ __forceinline__ int b_swz(int row) {
+  return WF == kMX4 ? (row >> 1) & 7 : row % 16;
+}
 static_assert(kBigTileRows == 128 && kTileRows == 64, "tile heights the B loader and fragments are laid out for");
 
 struct Bp {
-  const void* act;          // x [T][K] (gate/up, gathered by row_token) or h [R][K] (down), bf16
+  const void* act;          // x [T][K] (gate/up, gathered by row_token) or h [R][K] (down), bf16 (MX: E4M3)
+  const uint8_t* act_scale; // MX: E8M0 bytes [rows][K / 32] of act
   const int32_t* row_token;
   const int32_t* sched;
   const void* w;
   const void* w_scale;
   const void* w_min;
-  void* out;                // h [R][N] or y [R][N], bf16
+  void* out;                // h [R][N] or y [R][N], bf16 (MX: fp32)
   int K, N, T, R;
 };
 
@@ -100,19 +125,29 @@ __device__ __forceinline__ uint32_t gload_u16(const void* base, uint32_t off) {
   asm volatile("global_load_ushort %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
   return r;
 }
+__device__ __forceinline__ uint32_t gload_u8(const void* base, uint32_t off) {
+  uint32_t r;
+  asm volatile("global_load_ubyte %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
+  return r;
+}
 
-// Vector-memory loads each thread issues per super-stage (LDS DMA + A).
+// Vector-memory loads each thread issues per super-stage (LDS DMA + A; MX:
+// + one DMA of token scale bytes).
 template <int WF, int BM>
-constexpr int loads_per_stage() { return b_dma_per_wave<BM>() + (WF == kQ4 ? 4 + 8 : 16); }
+constexpr int loads_per_stage() {
+  return b_dma_per_wave<WF, BM>() + (WF == kQ4 ? 4 + 8 : WF == kMX4 ? 4 + 4 + 1 : 16);
+}
 
 // One wave's A operand for one super-stage: 4 fragments of 16 weight rows.
 //   4-bit: lane (r, q) holds the 16 bytes of block q of the super-stage
 //          (codes k = 32q .. 32q+31) and that block's scale and min;
 //   bf16:  lane (r, q) holds, for step kk, elements k = 32kk + 8q .. +7.
+//   MX:    lane (r, q) holds the 16 bytes of block q (elements k = 32q .. 32q+31)
+//          and that block's E8M0 scale byte.
 template <int WF>
 struct ATile {
-  u32x4 v[4][WF == kQ4 ? 1 : 4];
-  uint32_t sc[4], mn[4];  // 4-bit only: fp16 bits
+  u32x4 v[4][WF == kQ4 || WF == kMX4 ? 1 : 4];
+  uint32_t sc[4], mn[4];  // 4-bit: fp16 bits; MX: sc = scale byte
 };
 
 // Part g (0..7) of one super-stage's A loads (the loads are spread over the
@@ -122,7 +157,13 @@ struct ATile {
 template <int WF, class Row>
 __device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row (&arow)[4], int S, int q, int g) {
   const int b = g / 2;
-  if constexpr (WF == kQ4 && sizeof(Row) == 4) {
+  if constexpr (WF == kMX4) {
+    static_assert(sizeof(Row) == 4, "MX weights use 32-bit offsets");
+    if (g % 2 == 0)
+      a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
+    else
+      a.sc[b] = gload_u8(p.w_scale, arow[b] * (uint32_t)(p.K / 32) + S * (kSK / 32) + q);
+  } else if constexpr (WF == kQ4 && sizeof(Row) == 4) {
     // 32-bit offsets (the launcher checks that the weights fit)
     const uint32_t blk2 = 2u * (arow[b] * (uint32_t)(p.K / 32) + S * (kSK / 32) + q);
     if (g % 2 == 0) {
@@ -152,25 +193,36 @@ __device__ __forceinline__ void tie(ATile<WF>& a) {
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
 #pragma unroll
-    for (int i = 0; i < (WF == kQ4 ? 1 : 4); ++i) asm volatile("" : "+v"(a.v[b][i]));
+    for (int i = 0; i < (WF == kQ4 || WF == kMX4 ? 1 : 4); ++i) asm volatile("" : "+v"(a.v[b][i]));
     if constexpr (WF == kQ4) asm volatile("" : "+v"(a.sc[b]), "+v"(a.mn[b]));
+    if constexpr (WF == kMX4) asm volatile("" : "+v"(a.sc[b]));
   }
 }
 
-// B operand of one super-stage -> LDS, DMA instruction i of the wave (n = BM / 16
-// per wave): it writes the 1 KB at (n wave + i) KB of the stage: rows
-// 4 (n wave + i) + lane / 16, chunk slot lane % 16, which holds the row's
-// chunk slot ^ (row % 16).
-template <int BM, class Src>
-__device__ __forceinline__ void load_b_part(uint8_t* stage, const void* act, const Src (&src)[b_dma_per_wave<BM>()],
-                                            int S, int wave, int i) {
-  constexpr int n = b_dma_per_wave<BM>();
+// B operand of one super-stage -> LDS, DMA instruction i of the wave (n per
+// wave): it writes the 1 KB at (n wave + i) KB of the stage: rows
+// RPD (n wave + i) + lane / (64 / RPD), chunk slot lane % (64 / RPD), which
+// holds the row's chunk slot ^ b_swz(row).
+template <int WF, int BM, class Src>
+__device__ __forceinline__ void load_b_part(uint8_t* stage, const void* act,
+                                            const Src (&src)[b_dma_per_wave<WF, BM>()], int S, int wave, int i) {
+  constexpr int n = b_dma_per_wave<WF, BM>();
   const uint8_t* g;
   if constexpr (sizeof(Src) == 4)
-    g = (const uint8_t*)act + (src[i] + (uint32_t)S * (kSK * 2));  // 32-bit byte offset
+    g = (const uint8_t*)act + (src[i] + (uint32_t)S * b_row_bytes<WF>());  // 32-bit byte offset
   else
-    g = (const uint8_t*)src[i] + (size_t)S * (kSK * 2);
+    g = (const uint8_t*)src[i] + (size_t)S * b_row_bytes<WF>();
   __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(stage + (n * wave + i) * 1024), 16, 0, 0);
+}
+
+// MX: the 4 scale bytes of the lane's token row for one super-stage -> the
+// scale area after the rows (row r at byte b_scale_off(r)).  Every lane is
+// active, so that each wave issues the same loads on every path.
+template <int BM>
+__device__ __forceinline__ void load_bscale_part(uint8_t* stage, const uint8_t* act_scale, uint32_t src, int S,
+                                                 int wave) {
+  __builtin_amdgcn_global_load_lds((const void*)(act_scale + src + (uint32_t)S * (kSK / 32)),
+                                   (lds_void*)(stage + BM * kSK + wave * 256), 4, 0, 0);
 }
 
 // Barrier between super-stages.  __syncthreads() would also fence the
@@ -186,8 +238,12 @@ __device__ __forceinline__ void stage_barrier() {
 }
 
 // Chunk (16 bytes = 8 K) of a token row that lane group q reads for step kk.
+// MX: kk = 0 / 1 are the two halves of the FP8 operand (K 16q .. 16q+15 and
+// 64+16q .. 64+16q+15 of the super-stage: chunks q and 4 + q).
 template <int WF>
-__device__ __forceinline__ int b_chunk(int q, int kk) { return WF == kQ4 ? 4 * q + kk : 4 * kk + q; }
+__device__ __forceinline__ int b_chunk(int q, int kk) {
+  return WF == kQ4 ? 4 * q + kk : WF == kMX4 ? 4 * kk + q : 4 * kk + q;
+}
 
 // A fragment of step kk for weight block b.  4-bit: the dword holds codes
 // 8kk .. 8kk+7 of the lane's block, two per byte (even code in the low nibble).
@@ -213,6 +269,39 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
                                         int q, IssuePart&& issue_part) {
   constexpr int NG = BM / 64, G = 4 * NG, PPG = 8 / G;  // groups per step, groups, load parts per group
   constexpr bool kLean = ring<WF>() == 2;
+  if constexpr (WF == kMX4) {
+    // One scaled MFMA per (weight block, token block): groups of GW token
+    // blocks, each reading its two FP8 halves and scale byte from LDS right
+    // before its 4 GW MFMAs (two blocks per CU cover the LDS latency).
+    constexpr int GW = 4, MG = BM / 16 / GW, MPPG = 8 / MG;
+    // Row 16c + lr of the stage: the swizzle depends on lr alone, so the three
+    // LDS addresses of a token block differ from block 0's by a constant.
+    const uint8_t* h0 = st + lr * b_row_bytes<WF>() + 16 * (b_chunk<WF>(q, 0) ^ b_swz<WF>(lr));
+    const uint8_t* h1 = st + lr * b_row_bytes<WF>() + 16 * (b_chunk<WF>(q, 1) ^ b_swz<WF>(lr));
+    const uint8_t* sp = st + b_data_bytes<WF, BM>() + b_scale_off<BM>(lr) + q;
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pp = 0; pp < MPPG; ++pp) issue_part(g * MPPG + pp);
+      u32x4 b0[GW], b1[GW];
+      uint32_t bs[GW];
+#pragma unroll
+      for (int i = 0; i < GW; ++i) {
+        const int c = GW * g + i;
+        b0[i] = *reinterpret_cast<const u32x4*>(h0 + c * 16 * b_row_bytes<WF>());
+        b1[i] = *reinterpret_cast<const u32x4*>(h1 + c * 16 * b_row_bytes<WF>());
+        bs[i] = sp[b_scale_off<BM>(16 * c + lr) - b_scale_off<BM>(lr)];  // a constant for each c
+      }
+#pragma unroll
+      for (int i = 0; i < GW; ++i)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          acc[b][GW * g + i] = mfma_mx4_mx8_16x16x128(a.v[b][0], a.sc[b], b0[i], b1[i], bs[i], acc[b][GW * g + i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
+  }
   Q4Block qs[4];
   if constexpr (WF == kQ4) {
 #pragma unroll
@@ -291,13 +380,15 @@ __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(
 // group `group` against token rows [row0, row0 + rows) (rows <= BM).
 template <int WF, bool kGU, int BM>
 __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, int row0, int rows, int n0) {
-  constexpr int kBStage = b_stage_bytes<BM>(), NC = BM / 16, NB = b_dma_per_wave<BM>();
+  constexpr int kBStage = b_stage_bytes<WF, BM>(), NC = BM / 16, NB = b_dma_per_wave<WF, BM>();
+  constexpr int kRPD = b_rows_per_dma<WF>(), kLPR = kWave / kRPD;  // rows per DMA, lanes per row
+  constexpr int kEB = WF == kMX4 ? 1 : 2;                            // bytes per token element
   const int t = threadIdx.x, lane = t % kWave;
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);  // uniform: keep it in a scalar register
   const int lr = lane % 16, q = lane / 16;
 
   constexpr int kRing = ring<WF>(), kAhead = kRing - 1;
-  constexpr bool k32 = kRing == 2;  // 32-bit offsets
+  constexpr bool k32 = kRing == 2 || WF == kMX4;  // 32-bit offsets
   using Row = typename std::conditional<k32, uint32_t, size_t>::type;
   using Src = typename std::conditional<k32, uint32_t, const uint8_t*>::type;
   // A rows of this wave's 4 fragments (GU: gate cols i0.., i0+16.., then the up rows).
@@ -315,16 +406,24 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   Src bsrc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int rr = 4 * (NB * wave + i) + lane / 16;
+    const int rr = kRPD * (NB * wave + i) + lane / kLPR;
     const int r = rr < rows ? row0 + rr : row0;
-    const int chunk = (lane % 16) ^ (rr % 16);
+    const int chunk = (lane % kLPR) ^ b_swz<WF>(rr);
     if constexpr (k32) {
       const uint32_t src_row = kGU ? (uint32_t)min(max(p.row_token[r], 0), p.T - 1) : (uint32_t)r;
-      bsrc[i] = src_row * (uint32_t)p.K * 2 + 16 * chunk;
+      bsrc[i] = src_row * (uint32_t)p.K * kEB + 16 * chunk;
     } else {
       const size_t src_row = kGU ? (size_t)min(max(p.row_token[r], 0), p.T - 1) : (size_t)r;
-      bsrc[i] = (const uint8_t*)p.act + src_row * (size_t)p.K * 2 + 16 * chunk;
+      bsrc[i] = (const uint8_t*)p.act + src_row * (size_t)p.K * kEB + 16 * chunk;
     }
+  }
+  // MX: source of this lane's token scale bytes (row BM / 4 * wave + lane % (BM / 4)).
+  uint32_t ssrc = 0;
+  if constexpr (WF == kMX4) {
+    const int rr = BM / 4 * wave + lane % (BM / 4);
+    const int r = rr < rows ? row0 + rr : row0;
+    const uint32_t src_row = kGU ? (uint32_t)min(max(p.row_token[r], 0), p.T - 1) : (uint32_t)r;
+    ssrc = src_row * (uint32_t)(p.K / 32);
   }
 
   f32x4 acc[4][NC];
@@ -344,7 +443,11 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   constexpr int L = loads_per_stage<WF, BM>();
   // Part g (0..7) of the loads of super-stage S into slot j.
   auto part = [&](int S, int j, int g) {
-    if (g < NB) load_b_part<BM>(lds + j * kBStage, p.act, bsrc, S, wave, g);
+    if (g < NB) load_b_part<WF, BM>(lds + j * kBStage, p.act, bsrc, S, wave, g);
+    if constexpr (WF == kMX4) {
+      static_assert(NB < 7, "the scale DMA takes part 7");
+      if (g == 7) load_bscale_part<BM>(lds + j * kBStage, p.act_scale, ssrc, S, wave);
+    }
     load_a_part<WF>(p, at[j], arow, S, q, g);
   };
   auto issue = [&](int S, int j) {
@@ -396,8 +499,18 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
         float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = silu_fast(acc[b][c][i]) * acc[b + 2][c][i];
-        u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
+        if constexpr (WF == kMX4) {
+          *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = f32x4{v[0], v[1], v[2], v[3]};
+        } else {
+          u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
+        }
+      }
+    } else if constexpr (WF == kMX4) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int col = n0 + 64 * wave + 16 * b + 4 * q;
+        *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = acc[b][c];
       }
     } else {
 #pragma unroll
@@ -410,6 +523,13 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   }
 }
 
+// Waves per SIMD (blocks per CU): bf16 one (three-deep ring, operand
+// prefetch), 4-bit two (see the top of the file).  MX: one -- its 64 x 128
+// fp32 accumulators per wave, two register slots of FP4 weights and the FP8
+// token fragments (8 registers each) do not fit in half the register file.
+template <int WF>
+constexpr int big_waves_per_simd() { return WF == kQ4 ? 2 : 1; }
+
 // One block per item.  Items of the big-tile list (128-row tiles) and, for
 // 4-bit weights, of the small-tile list (<= 64 rows) share the launch: block b
 // runs on XCD b % 8, and each XCD takes a contiguous run of the big items
@@ -417,9 +537,9 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
 // the CUs that the last big items leave idle, and the column blocks of one
 // row tile (which read the same token rows) share an L2.
 template <int WF, bool kGU, bool kSmall>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(ring<WF>() == 2 ? 2 : 1)))
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(big_waves_per_simd<WF>())))
 void big_gemm_kernel(Bp p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring<WF>() * b_stage_bytes<kBigTileRows>()];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring<WF>() * b_stage_bytes<WF, kBigTileRows>()];
   const int cols = kGU ? kBN / 2 : kBN;  // output columns per item
   const int per_tile = p.N / cols;
   const int big_items = p.sched[kSchedBig] * per_tile;
@@ -445,12 +565,14 @@ void big_gemm_kernel(Bp p) {
 // vmcnt accounting of the ring: the build's assembly check rejects it.
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
-  if (a.wfmt != kBF16 && a.wfmt != kQ4) return hipErrorInvalidValue;
-  // bf16 small tiles keep the K-split kernel; 4-bit small tiles always run here
-  if (with_small != (a.wfmt == kQ4)) return hipErrorInvalidValue;
+  if (a.wfmt != kBF16 && a.wfmt != kQ4 && a.wfmt != kMX4) return hipErrorInvalidValue;
+  // bf16 small tiles keep the K-split kernel; 4-bit and MX small tiles always run here
+  if (with_small != (a.wfmt != kBF16)) return hipErrorInvalidValue;
   const int cols = kGU ? kBN / 2 : kBN;
   if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
-  Bp p{a.act, a.row_token, a.sched, a.w, a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
+  const bool mx = a.wfmt == kMX4;
+  Bp p{mx ? (const void*)a.act_q : a.act, mx ? (const uint8_t*)a.act_scale : nullptr, a.row_token, a.sched, a.w,
+       a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
   // grid: per XCD, slots for an upper bound of each list's items (big tiles
   // hold >= kBigPartMin rows)
   const int64_t per_tile = a.N / cols;
@@ -458,7 +580,9 @@ hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   const int64_t small_px = with_small ? ((int64_t)sched_small_cap(a.R, a.G) * per_tile + kXcds - 1) / kXcds : 0;
   const int64_t blocks = (big_px + small_px) * kXcds;
   if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
-  if (with_small)
+  if (mx)
+    hipLaunchKernelGGL((big_gemm_kernel<kMX4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+  else if (with_small)
     hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
   else
     hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU, false>), dim3(blocks), dim3(kThreads), 0, stream, p);

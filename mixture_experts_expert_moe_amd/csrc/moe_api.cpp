@@ -74,14 +74,25 @@ bool q4_offsets_fit(const moe_desc* d) {
   return G * 2 * I * (H / 2) < lim && (int64_t)d->max_tokens * H * 2 < lim && r_max * I * 2 < lim;
 }
 
-bool big_tiles(const moe_desc* d, int32_t T) {
-  if (T < moe::kBigTileMinTokens) return false;
-  return d->w_dtype == MOE_BF16 || (d->w_dtype == MOE_Q4B32 && q4_offsets_fit(d));
+// The same for MXFP4 weights (E4M3 activations: one byte per element).
+bool mx_offsets_fit(const moe_desc* d) {
+  const int64_t H = d->hidden, I = d->inter, G = d->n_routed + d->n_shared;
+  const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
+  const int64_t lim = (int64_t)1 << 32;
+  return G * 2 * I * (H / 2) < lim && (int64_t)d->max_tokens * H < lim && r_max * I < lim;
 }
 
-// With big tiles on, the small tiles of 4-bit weights go through the
-// register-dequant kernel in the same launch as the big tiles.
-bool q4_small_reg(const moe_desc* d, int32_t T) { return d->w_dtype == MOE_Q4B32 && big_tiles(d, T); }
+bool big_tiles(const moe_desc* d, int32_t T) {
+  if (T < moe::kBigTileMinTokens) return false;
+  return d->w_dtype == MOE_BF16 || (d->w_dtype == MOE_Q4B32 && q4_offsets_fit(d)) ||
+         (d->w_dtype == MOE_MXFP4 && mx_offsets_fit(d));
+}
+
+// With big tiles on, the small tiles of 4-bit and MX weights go through the
+// big-tile kernel too, in the same launch as the big tiles.
+bool q4_small_reg(const moe_desc* d, int32_t T) {
+  return (d->w_dtype == MOE_Q4B32 || d->w_dtype == MOE_MXFP4) && big_tiles(d, T);
+}
 
 moe_status check_weights(const moe_desc* d, const moe_weights* w) {
   if (!w || !ptr_ok(w->w)) return MOE_ERR_INVALID_ARG;
