@@ -328,7 +328,7 @@ def stack_figures():
     return out
 
 
-def mx4_figures(args):
+def mx4_figures(args, decode=True):
     """MXFP4 weights x MXFP8 activations: the T=2048 Zipf prefill (MFMA fraction
     against the fp8 peak) and decode steps T = 1, 2, 4, 8 (HBM fraction of the
     two GEMM launches, which read the touched groups' 4.25-bit weights)."""
@@ -350,6 +350,8 @@ def mx4_figures(args):
     }
     del rq
     torch.cuda.empty_cache()
+    if not decode:
+        return out
     sweep = {}
     for Td in (1, 2, 4, 8):
         rd = Runner("mx4_e128_top8_shared", Td, args.rotations, args.steps + args.warmup)
@@ -381,8 +383,8 @@ def main():
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer 4-bit stack figures")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
     ap.add_argument("--workloads", default="headline,decode,fp32,q4,mx4,stack",
-                    help="comma list of the parts to run (profiling runs pick one); without 'headline' the line's "
-                         "value is null")
+                    help="comma list of the parts to run (profiling runs pick one; mx4p: the MX prefill only); "
+                         "without 'headline' the line's value is null")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a reference kernel of known "
                          "size for hardware-counter calibration)")
@@ -502,8 +504,8 @@ def main():
         del rq
         torch.cuda.empty_cache()
 
-    if "mx4" in parts:
-        extra.update(mx4_figures(args))
+    if "mx4" in parts or "mx4p" in parts:
+        extra.update(mx4_figures(args, decode="mx4" in parts))
         torch.cuda.empty_cache()
 
     if not args.no_stack:

@@ -30,10 +30,12 @@
 // products unchanged.
 // MXFP4 weights (E2M1, one E8M0 scale per 32) against MXFP8 token rows take
 // the same loop with one scaled FP4 x FP8 MFMA (16x16x128) per fragment pair
-// and super-stage: a lane's 16-byte weight load is its whole 32-element block
-// plus one scale byte, nothing is decoded, the token rows are 128 bytes per
-// super-stage in LDS, and their scale bytes (4 per row) are copied into LDS
-// next to them by the same DMA.
+// and super-stage: a lane's 16-byte weight load is its whole 32-element block,
+// nothing is decoded, and the token rows are 128 bytes per super-stage in LDS.
+// The scale bytes of the item's 256 weight rows and of its token rows (K / 32
+// per row) are copied into LDS once, in 16-byte chunks, before the loop: read
+// per super-stage from global memory, one byte per lane, they were half of the
+// cache lines the loop touched and held its load issue back.
 //
 // The shared expert and every routed expert go through the same launch; the
 // grouping itself is the point of the pages' "concatenated-expert" fix
@@ -58,9 +60,13 @@ constexpr int kSK = 128;                 // K per super-stage
 #ifndef MOE_BIG_RING_Q4
 #define MOE_BIG_RING_Q4 2
 #endif
+#ifndef MOE_BIG_RING_MX
+#define MOE_BIG_RING_MX 4
+#endif
 template <int WF>
-constexpr int ring() { return WF == kQ4 ? MOE_BIG_RING_Q4 : 3; }
+constexpr int ring() { return WF == kQ4 ? MOE_BIG_RING_Q4 : WF == kMX4 ? MOE_BIG_RING_MX : 3; }
 static_assert(MOE_BIG_RING_Q4 == 2 || MOE_BIG_RING_Q4 == 3, "ring depth");
+static_assert(MOE_BIG_RING_MX >= 3 && MOE_BIG_RING_MX <= 4, "ring depth");
 constexpr int kThreads = 256;
 // Token rows per block: kBigTileRows for the big-tile list, kTileRows for the
 // small-tile list.  Bytes of one token row per super-stage (bf16: 256, E4M3:
@@ -74,10 +80,16 @@ template <int WF, int BM> constexpr int b_data_bytes() { return BM * b_row_bytes
 // MX scale area: each wave's DMA writes 64 dwords (256 bytes); lane l of wave
 // w holds the 4 scale bytes of token row BM / 4 * w + l % (BM / 4) (lanes
 // past BM / 4 repeat rows, so that every lane of the DMA is active).
-template <int WF, int BM> constexpr int b_stage_bytes() { return b_data_bytes<WF, BM>() + (WF == kMX4 ? 1024 : 0); }
-template <int BM> __device__ __forceinline__ constexpr int b_scale_off(int row) {
-  return 256 * (row / (BM / 4)) + 4 * (row % (BM / 4));
-}
+template <int WF, int BM> constexpr int b_stage_bytes() { return b_data_bytes<WF, BM>(); }
+// MX item scales in LDS (K <= kMxMaxK, K % 512 == 0): the 256 weight rows'
+// bytes, then the token rows', each row K / 32 bytes.  DMA instructions per
+// wave: weight rows 256 K / 512 chunks of 16 bytes over 4 waves x 64 lanes;
+// token rows BM K / 512 chunks (at least one instruction per wave; lanes past
+// the last chunk repeat it into the padding).
+constexpr int kMxMaxK = 2048;
+constexpr int kMxScaleBytes = kBN * (kMxMaxK / 32) + kBigTileRows * (kMxMaxK / 32);
+__device__ __forceinline__ int mx_a_dma(int K) { return K / 512; }
+template <int BM> __device__ __forceinline__ int mx_b_dma(int K) { return max(1, BM * (K / 512) / 256); }
 template <int WF, int BM> constexpr int b_dma_per_wave() { return b_data_bytes<WF, BM>() / 1024 / 4; }
 // Chunk slot of a row's 16-byte chunk c in LDS: XOR-swizzled by row so that
 // the 16 rows of a fragment read spread over the banks (256-byte rows: all
@@ -125,29 +137,25 @@ __device__ __forceinline__ uint32_t gload_u16(const void* base, uint32_t off) {
   asm volatile("global_load_ushort %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
   return r;
 }
-__device__ __forceinline__ uint32_t gload_u8(const void* base, uint32_t off) {
-  uint32_t r;
-  asm volatile("global_load_ubyte %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
-  return r;
-}
+
 
 // Vector-memory loads each thread issues per super-stage (LDS DMA + A; MX:
 // + one DMA of token scale bytes).
 template <int WF, int BM>
 constexpr int loads_per_stage() {
-  return b_dma_per_wave<WF, BM>() + (WF == kQ4 ? 4 + 8 : WF == kMX4 ? 4 + 4 + 1 : 16);
+  return b_dma_per_wave<WF, BM>() + (WF == kQ4 ? 4 + 8 : WF == kMX4 ? 4 : 16);
 }
 
 // One wave's A operand for one super-stage: 4 fragments of 16 weight rows.
 //   4-bit: lane (r, q) holds the 16 bytes of block q of the super-stage
 //          (codes k = 32q .. 32q+31) and that block's scale and min;
 //   bf16:  lane (r, q) holds, for step kk, elements k = 32kk + 8q .. +7.
-//   MX:    lane (r, q) holds the 16 bytes of block q (elements k = 32q .. 32q+31)
-//          and that block's E8M0 scale byte.
+//   MX:    lane (r, q) holds the 16 bytes of block q (elements k = 32q .. 32q+31);
+//          the scale bytes are in LDS.
 template <int WF>
 struct ATile {
   u32x4 v[4][WF == kQ4 || WF == kMX4 ? 1 : 4];
-  uint32_t sc[4], mn[4];  // 4-bit: fp16 bits; MX: sc = scale byte
+  uint32_t sc[4], mn[4];  // 4-bit only: fp16 bits
 };
 
 // Part g (0..7) of one super-stage's A loads (the loads are spread over the
@@ -159,10 +167,7 @@ __device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row
   const int b = g / 2;
   if constexpr (WF == kMX4) {
     static_assert(sizeof(Row) == 4, "MX weights use 32-bit offsets");
-    if (g % 2 == 0)
-      a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
-    else
-      a.sc[b] = gload_u8(p.w_scale, arow[b] * (uint32_t)(p.K / 32) + S * (kSK / 32) + q);
+    if (g % 2 == 0) a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
   } else if constexpr (WF == kQ4 && sizeof(Row) == 4) {
     // 32-bit offsets (the launcher checks that the weights fit)
     const uint32_t blk2 = 2u * (arow[b] * (uint32_t)(p.K / 32) + S * (kSK / 32) + q);
@@ -195,7 +200,6 @@ __device__ __forceinline__ void tie(ATile<WF>& a) {
 #pragma unroll
     for (int i = 0; i < (WF == kQ4 || WF == kMX4 ? 1 : 4); ++i) asm volatile("" : "+v"(a.v[b][i]));
     if constexpr (WF == kQ4) asm volatile("" : "+v"(a.sc[b]), "+v"(a.mn[b]));
-    if constexpr (WF == kMX4) asm volatile("" : "+v"(a.sc[b]));
   }
 }
 
@@ -215,14 +219,9 @@ __device__ __forceinline__ void load_b_part(uint8_t* stage, const void* act,
   __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(stage + (n * wave + i) * 1024), 16, 0, 0);
 }
 
-// MX: the 4 scale bytes of the lane's token row for one super-stage -> the
-// scale area after the rows (row r at byte b_scale_off(r)).  Every lane is
-// active, so that each wave issues the same loads on every path.
-template <int BM>
-__device__ __forceinline__ void load_bscale_part(uint8_t* stage, const uint8_t* act_scale, uint32_t src, int S,
-                                                 int wave) {
-  __builtin_amdgcn_global_load_lds((const void*)(act_scale + src + (uint32_t)S * (kSK / 32)),
-                                   (lds_void*)(stage + BM * kSK + wave * 256), 4, 0, 0);
+// MX: one 16-byte chunk of item scales -> LDS (lane-consecutive destinations).
+__device__ __forceinline__ void load_scale_chunk(uint8_t* dst, const uint8_t* src) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
 }
 
 // Barrier between super-stages.  __syncthreads() would also fence the
@@ -264,41 +263,62 @@ __device__ __forceinline__ u32x4 a_frag(const ATile<WF>& a, const Q4Block (&qs)[
 // loads of a later super-stage (issue_part(p)) are spread evenly over the
 // groups, so that the memory pipeline fills while the MFMAs run instead of in
 // one burst.  sched_barrier pins that order.
+// MX scale bytes of one super-stage in LDS: a[b] = this lane's byte for
+// weight fragment b (its row, block 4 S + q), b = token block 0's (row lr),
+// token block c's at b + c * bstep.
+struct MxSc {
+  const uint8_t* a[4];
+  const uint8_t* b;
+  int bstep;
+};
+
 template <int WF, int BM, class IssuePart>
 __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[4][BM / 16], int lr,
-                                        int q, IssuePart&& issue_part) {
+                                        int q, IssuePart&& issue_part, const MxSc& sc = MxSc{}) {
   constexpr int NG = BM / 64, G = 4 * NG, PPG = 8 / G;  // groups per step, groups, load parts per group
   constexpr bool kLean = ring<WF>() == 2;
   if constexpr (WF == kMX4) {
-    // One scaled MFMA per (weight block, token block): groups of GW token
-    // blocks, each reading its two FP8 halves and scale byte from LDS right
-    // before its 4 GW MFMAs (two blocks per CU cover the LDS latency).
+    // One scaled MFMA per (weight block, token block), in groups of GW token
+    // blocks; the next group's two FP8 halves and scale bytes are read from
+    // LDS before the current group's 4 GW MFMAs are issued (one wave per
+    // SIMD: nothing else would cover the LDS latency).
     constexpr int GW = 4, MG = BM / 16 / GW, MPPG = 8 / MG;
-    // Row 16c + lr of the stage: the swizzle depends on lr alone, so the three
-    // LDS addresses of a token block differ from block 0's by a constant.
+    // Row 16c + lr of the stage: the swizzle depends on lr alone, so the LDS
+    // addresses of a token block differ from block 0's by a constant.
     const uint8_t* h0 = st + lr * b_row_bytes<WF>() + 16 * (b_chunk<WF>(q, 0) ^ b_swz<WF>(lr));
     const uint8_t* h1 = st + lr * b_row_bytes<WF>() + 16 * (b_chunk<WF>(q, 1) ^ b_swz<WF>(lr));
-    const uint8_t* sp = st + b_data_bytes<WF, BM>() + b_scale_off<BM>(lr) + q;
+    uint32_t as[4];
 #pragma unroll
-    for (int g = 0; g < MG; ++g) {
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int pp = 0; pp < MPPG; ++pp) issue_part(g * MPPG + pp);
+    for (int b = 0; b < 4; ++b) as[b] = *sc.a[b];
+    struct BG {
       u32x4 b0[GW], b1[GW];
       uint32_t bs[GW];
+    };
+    auto read_group = [&](BG& o, int g) {
 #pragma unroll
       for (int i = 0; i < GW; ++i) {
         const int c = GW * g + i;
-        b0[i] = *reinterpret_cast<const u32x4*>(h0 + c * 16 * b_row_bytes<WF>());
-        b1[i] = *reinterpret_cast<const u32x4*>(h1 + c * 16 * b_row_bytes<WF>());
-        bs[i] = sp[b_scale_off<BM>(16 * c + lr) - b_scale_off<BM>(lr)];  // a constant for each c
+        o.b0[i] = *reinterpret_cast<const u32x4*>(h0 + c * 16 * b_row_bytes<WF>());
+        o.b1[i] = *reinterpret_cast<const u32x4*>(h1 + c * 16 * b_row_bytes<WF>());
+        o.bs[i] = sc.b[c * sc.bstep];
       }
+    };
+    BG cur, nxt;
+    read_group(cur, 0);
+#pragma unroll
+    for (int g = 0; g < MG; ++g) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (g + 1 < MG) read_group(nxt, g + 1);
+#pragma unroll
+      for (int pp = 0; pp < MPPG; ++pp) issue_part(g * MPPG + pp);
 #pragma unroll
       for (int i = 0; i < GW; ++i)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
-          acc[b][GW * g + i] = mfma_mx4_mx8_16x16x128(a.v[b][0], a.sc[b], b0[i], b1[i], bs[i], acc[b][GW * g + i]);
+          acc[b][GW * g + i] =
+              mfma_mx4_mx8_16x16x128(a.v[b][0], as[b], cur.b0[i], cur.b1[i], cur.bs[i], acc[b][GW * g + i]);
       __builtin_amdgcn_sched_barrier(0);
+      if (g + 1 < MG) cur = nxt;
     }
     return;
   }
@@ -417,14 +437,51 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
       bsrc[i] = (const uint8_t*)p.act + src_row * (size_t)p.K * kEB + 16 * chunk;
     }
   }
-  // MX: source of this lane's token scale bytes (row BM / 4 * wave + lane % (BM / 4)).
-  uint32_t ssrc = 0;
+  // MX: the item's scale bytes -> LDS after the ring (weight rows, then token
+  // rows; K / 32 bytes per row, 16-byte chunks, lane-consecutive), issued
+  // before the first super-stage's loads, so the first wait covers them.
+  uint8_t* const asc_lds = lds + kRing * b_stage_bytes<WF, kBigTileRows>();
+  uint8_t* const bsc_lds = asc_lds + kBN * (kMxMaxK / 32);
+  const int kpr = p.K / 32;
   if constexpr (WF == kMX4) {
-    const int rr = BM / 4 * wave + lane % (BM / 4);
-    const int r = rr < rows ? row0 + rr : row0;
-    const uint32_t src_row = kGU ? (uint32_t)min(max(p.row_token[r], 0), p.T - 1) : (uint32_t)r;
-    ssrc = src_row * (uint32_t)(p.K / 32);
+    const int cpr = p.K / 512, na = mx_a_dma(p.K), nb = mx_b_dma<BM>(p.K);
+#pragma unroll
+    for (int i = 0; i < kMxMaxK / 512; ++i) {
+      if (i < na) {
+        const int ci = (wave * na + i) * kWave + lane;  // < 256 cpr
+        const int lw = ci / cpr, part = ci % cpr;
+        const uint32_t grow = kGU ? (uint32_t)group * 2 * p.N + (lw < 128 ? n0 + lw : p.N + n0 + lw - 128)
+                                  : (uint32_t)group * p.N + n0 + lw;
+        load_scale_chunk(asc_lds + (wave * na + i) * 1024,
+                         (const uint8_t*)p.w_scale + grow * (uint32_t)kpr + 16 * part);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBigTileRows * (kMxMaxK / 512) / 256; ++i) {
+      if (i < nb) {
+        const int ci = min((wave * nb + i) * kWave + lane, BM * cpr - 1);
+        const int rr = ci / cpr, part = ci % cpr;
+        const int r = rr < rows ? row0 + rr : row0;
+        const uint32_t src_row = kGU ? (uint32_t)min(max(p.row_token[r], 0), p.T - 1) : (uint32_t)r;
+        load_scale_chunk(bsc_lds + (wave * nb + i) * 1024, p.act_scale + src_row * (uint32_t)kpr + 16 * part);
+      }
+    }
   }
+  // MX: this lane's scale bytes of super-stage S (block 4 S + q): weight
+  // fragment b's row, token block 0's row (lr); token block c at + 16 c kpr.
+  auto mx_sc = [&](int S) {
+    MxSc sc{};
+    if constexpr (WF == kMX4) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int lw = kGU ? (b < 2 ? 0 : 128) + 32 * wave + 16 * (b & 1) + lr : 64 * wave + 16 * b + lr;
+        sc.a[b] = asc_lds + lw * kpr + 4 * S + q;
+      }
+      sc.b = bsc_lds + lr * kpr + 4 * S + q;
+      sc.bstep = 16 * kpr;
+    }
+    return sc;
+  };
 
   f32x4 acc[4][NC];
 #pragma unroll
@@ -444,10 +501,6 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   // Part g (0..7) of the loads of super-stage S into slot j.
   auto part = [&](int S, int j, int g) {
     if (g < NB) load_b_part<WF, BM>(lds + j * kBStage, p.act, bsrc, S, wave, g);
-    if constexpr (WF == kMX4) {
-      static_assert(NB < 7, "the scale DMA takes part 7");
-      if (g == 7) load_bscale_part<BM>(lds + j * kBStage, p.act_scale, ssrc, S, wave);
-    }
     load_a_part<WF>(p, at[j], arow, S, q, g);
   };
   auto issue = [&](int S, int j) {
@@ -456,29 +509,36 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   };
   issue(0, 0);
   if constexpr (kAhead > 1) issue(min(1, nS - 1), 1);
+  if constexpr (kAhead > 2) issue(min(2, nS - 1), 2);
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * (kAhead - 1)) : "memory");  // super-stage 0 landed
   tie<WF>(at[0]);
   stage_barrier();
   auto step = [&](int S, auto slot) {
     constexpr int j = decltype(slot)::value;
     const int S2 = min(S + kAhead, nS - 1);
-    compute<WF, BM>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) { part(S2, (j + kAhead) % kRing, g); });
+    compute<WF, BM>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) { part(S2, (j + kAhead) % kRing, g); },
+                    mx_sc(S));
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * (kAhead - 1)) : "memory");  // super-stage S + 1 landed
     tie<WF>(at[(j + 1) % kRing]);
     stage_barrier();
   };
-  // Whole rounds of the ring, then the remaining one or two super-stages
-  // (nested, so that every path through the waits is one the ring takes).
+  // Whole rounds of the ring, then the remaining super-stages (fewer than
+  // kRing; nested, so that every path through the waits is one the ring takes).
   int S = 0;
   for (; S + kRing <= nS; S += kRing) {
     step(S, std::integral_constant<int, 0>{});
     step(S + 1, std::integral_constant<int, 1>{});
     if constexpr (kRing > 2) step(S + 2, std::integral_constant<int, 2 % kRing>{});
+    if constexpr (kRing > 3) step(S + 3, std::integral_constant<int, 3 % kRing>{});
   }
   if (S < nS) {
     step(S, std::integral_constant<int, 0>{});
     if constexpr (kRing > 2)
-      if (S + 1 < nS) step(S + 1, std::integral_constant<int, 1>{});
+      if (S + 1 < nS) {
+        step(S + 1, std::integral_constant<int, 1>{});
+        if constexpr (kRing > 3)
+          if (S + 2 < nS) step(S + 2, std::integral_constant<int, 2 % kRing>{});
+      }
   }
   // Drain the last (clamped) refills.  Their registers are tied after the wait
   // so that the compiler keeps them reserved until the loads have landed.
@@ -539,7 +599,8 @@ constexpr int big_waves_per_simd() { return WF == kQ4 ? 2 : 1; }
 template <int WF, bool kGU, bool kSmall>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(big_waves_per_simd<WF>())))
 void big_gemm_kernel(Bp p) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[ring<WF>() * b_stage_bytes<WF, kBigTileRows>()];
+  __shared__ __attribute__((aligned(1024)))
+  uint8_t lds[ring<WF>() * b_stage_bytes<WF, kBigTileRows>() + (WF == kMX4 ? kMxScaleBytes : 0)];
   const int cols = kGU ? kBN / 2 : kBN;  // output columns per item
   const int per_tile = p.N / cols;
   const int big_items = p.sched[kSchedBig] * per_tile;
@@ -571,6 +632,7 @@ hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   const int cols = kGU ? kBN / 2 : kBN;
   if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
   const bool mx = a.wfmt == kMX4;
+  if (mx && (a.K % 512 != 0 || a.K > kMxMaxK)) return hipErrorInvalidValue;
   Bp p{mx ? (const void*)a.act_q : a.act, mx ? (const uint8_t*)a.act_scale : nullptr, a.row_token, a.sched, a.w,
        a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
   // grid: per XCD, slots for an upper bound of each list's items (big tiles

@@ -74,8 +74,11 @@ bool q4_offsets_fit(const moe_desc* d) {
   return G * 2 * I * (H / 2) < lim && (int64_t)d->max_tokens * H * 2 < lim && r_max * I * 2 < lim;
 }
 
-// The same for MXFP4 weights (E4M3 activations: one byte per element).
+// The same for MXFP4 weights (E4M3 activations: one byte per element); the MX
+// big-tile kernel also keeps an item's scale bytes in LDS, which takes
+// hidden and inter multiples of 512 up to 2048.
 bool mx_offsets_fit(const moe_desc* d) {
+  if (d->hidden % 512 || d->inter % 512 || d->hidden > 2048 || d->inter > 2048) return false;
   const int64_t H = d->hidden, I = d->inter, G = d->n_routed + d->n_shared;
   const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
   const int64_t lim = (int64_t)1 << 32;

@@ -64,6 +64,10 @@ SMALL = [
     ("mx4_e16k4s1_t37", 256, 256, 16, 4, 1, 37, "mx4", 0.0),
     ("mx4_e16k2s1_t200_zipf", 512, 256, 16, 2, 1, 200, "mx4", 1.1),
     ("mx4_e8k2s1_t1100", 256, 256, 8, 2, 1, 1100, "mx4", 0.0),
+    # MX big tiles (hidden and inter multiples of 512 up to 2048): one and two
+    # 16-byte scale chunks per row in the item's LDS copy, Zipf-skewed groups
+    ("mx4_e8k2s1_t1100_h512_big", 512, 512, 8, 2, 1, 1100, "mx4", 0.0),
+    ("mx4_e16k4s1_t1024_h1024_zipf_big", 1024, 1024, 16, 4, 1, 1024, "mx4", 1.1),
 ]
 
 
