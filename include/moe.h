@@ -10,6 +10,7 @@
  *   moe_grouped_gemm_down one launch: down GEMM of every expert
  *   moe_combine           gate-weighted, atomic-free sum of each token's rows
  *   moe_combine_rmsnorm   the same, plus the RMSNorm of the result (stacked layers)
+ *   (helpers: moe_rmsnorm, moe_quant_mx8)
  *
  * or, for a few tokens (decode steps), one call for all of it:
  *
@@ -279,6 +280,18 @@ moe_status moe_decode_layer_static(const moe_desc* desc, int32_t T, const void* 
                                    const float* bias, const moe_weights* w_gu, const moe_weights* w_down,
                                    const float* residual, int32_t flags, float eps, void* out,
                                    hipStream_t stream);
+
+/* MXFP8 quantisation (OCP MX: E4M3 elements, one E8M0 scale byte per 32 consecutive
+ * values of a row), the conversion moe_permute applies to x and moe_grouped_gemm_down
+ * to h for MXFP4 weights: block maximum m = max |v|; scale byte = clamp(floor(log2 m)
+ * - 8 + 127, 0, 254) (8: the exponent of 448, the largest E4M3 value), or 0 when
+ * m = 0; code = the E4M3 value nearest v / 2^(byte - 127), ties to the even mantissa,
+ * magnitudes above 448 saturated to 448, 0 for an all-zero block.
+ *   src:    [rows][cols] fp32 (src_dtype MOE_F32) or bf16 (MOE_BF16)
+ *   codes:  [rows][cols] E4M3 bytes;  scales: [rows][cols / 32] E8M0 bytes
+ * cols % 256 == 0 (else MOE_ERR_UNSUPPORTED); src and codes 16-byte aligned. */
+moe_status moe_quant_mx8(int64_t rows, int32_t cols, int32_t src_dtype, const void* src, uint8_t* codes,
+                         uint8_t* scales, hipStream_t stream);
 
 /* RMSNorm with unit gain for stacked layers: xn[t] = bf16(x[t] / sqrt(mean(x[t]^2) + eps)),
  * computed in fp32.  x: [T][H] fp32; xn: [T][H] bf16.  H % 256 == 0. */

@@ -438,6 +438,16 @@ moe_status moe_decode_layer_static(const moe_desc* d, int32_t T, const void* x, 
   return moe_decode_layer(&ds, T, x, w_router, bias, w_gu, w_down, residual, flags, eps, out, &b, stream);
 }
 
+moe_status moe_quant_mx8(int64_t rows, int32_t cols, int32_t src_dtype, const void* src, uint8_t* codes,
+                         uint8_t* scales, hipStream_t stream) {
+  if (rows < 0 || cols <= 0 || (src_dtype != MOE_F32 && src_dtype != MOE_BF16)) return MOE_ERR_INVALID_ARG;
+  if (cols % 256) return MOE_ERR_UNSUPPORTED;
+  if (!ptr_ok(src) || !ptr_ok(codes) || !scales) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if ((uint64_t)rows * (uint64_t)cols / 2048 + 1 > (uint64_t)INT32_MAX) return MOE_ERR_UNSUPPORTED;
+  return hip_status(moe::launch_quant_mx8_rows(src, src_dtype == MOE_F32, codes, scales, rows, cols, stream));
+}
+
 moe_status moe_rmsnorm(int32_t T, int32_t H, float eps, const float* x, void* xn, hipStream_t stream) {
   if (T < 0 || H <= 0 || !(eps >= 0.0f)) return MOE_ERR_INVALID_ARG;
   if (H % 256) return MOE_ERR_UNSUPPORTED;

@@ -20,7 +20,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED", -3:
 
 # The C-ABI entry points declared in include/moe.h.
 EXPORTS = ("moe_buffer_sizes", "moe_route_topk", "moe_permute", "moe_route_permute", "moe_grouped_gemm_gu",
-           "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_decode_layer",
+           "moe_grouped_gemm_down", "moe_combine", "moe_combine_rmsnorm", "moe_rmsnorm", "moe_quant_mx8",
+           "moe_decode_layer",
            "moe_decode_layer_static", "moe_status_string", "moe_abi_version")
 
 
@@ -69,6 +70,7 @@ def lib():
         L.moe_combine.argtypes = [P(MoeDesc), i32, vp, vp, P(MoeBuffers), vp]
         L.moe_combine_rmsnorm.argtypes = [P(MoeDesc), i32, vp, ctypes.c_float, vp, vp, P(MoeBuffers), vp]
         L.moe_rmsnorm.argtypes = [i32, i32, ctypes.c_float, vp, vp, vp]
+        L.moe_quant_mx8.argtypes = [ctypes.c_int64, i32, i32, vp, vp, vp, vp]
         L.moe_decode_layer.argtypes = [P(MoeDesc), i32, vp, vp, vp, P(MoeWeights), P(MoeWeights), vp, i32,
                                        ctypes.c_float, vp, P(MoeBuffers), vp]
         L.moe_decode_layer_static.argtypes = [P(MoeDesc), i32, vp, vp, vp, P(MoeWeights), P(MoeWeights), vp, i32,
@@ -195,6 +197,12 @@ def sync_status(tensors: dict) -> int:
 
 def moe_rmsnorm(T, H, eps, x, xn, stream=None):
     _check("moe_rmsnorm", lib().moe_rmsnorm(T, H, eps, _ptr(x), _ptr(xn), _stream(stream)))
+
+
+def moe_quant_mx8(rows, cols, src_dtype, src, codes, scales, stream=None):
+    """MXFP8 of rows x cols values (src_dtype "f32" or "bf16") into E4M3 codes and E8M0 scales."""
+    _check("moe_quant_mx8", lib().moe_quant_mx8(rows, cols, DTYPE_CODE[src_dtype], _ptr(src), _ptr(codes),
+                                                _ptr(scales), _stream(stream)))
 
 
 class MoeLayer:

@@ -189,3 +189,16 @@ def test_decode_layer_static_rejects_before_launch():
     assert call(d, -1) == -1
     assert call(d, 17) == -2                    # the static buffers are laid out for 16 tokens
     assert call(desc(hidden=2000), 1) == -2
+
+
+def test_quant_mx8_rejects_before_launch():
+    L = moe.lib()
+    q = L.moe_quant_mx8
+    assert q(0, 256, moe.MOE_F32, FAKE, FAKE, FAKE, None) == 0          # no rows: no work
+    assert q(-1, 256, moe.MOE_F32, FAKE, FAKE, FAKE, None) == -1
+    assert q(4, 0, moe.MOE_F32, FAKE, FAKE, FAKE, None) == -1
+    assert q(4, 256, moe.MOE_I8, FAKE, FAKE, FAKE, None) == -1          # source must be fp32 or bf16
+    assert q(4, 320, moe.MOE_BF16, FAKE, FAKE, FAKE, None) == -2        # cols % 256
+    assert q(4, 256, moe.MOE_F32, None, FAKE, FAKE, None) == -1
+    assert q(4, 256, moe.MOE_F32, FAKE, FAKE + 8, FAKE, None) == -1     # codes misaligned
+    assert q(4, 256, moe.MOE_F32, FAKE, FAKE, None, None) == -1

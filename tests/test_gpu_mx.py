@@ -1,6 +1,7 @@
 """MXFP8 block quantisation on the GPU (E4M3 elements, one E8M0 scale byte
 per 32 values), the step in front of the scaled FP4 x FP8 MFMA: x (bf16)
-inside moe_permute, h (fp32) inside moe_grouped_gemm_down.  Codes and scale
+inside moe_permute, h (fp32) inside moe_grouped_gemm_down, and any fp32 or
+bf16 rows through moe_quant_mx8 (the same kernel).  Codes and scale
 bytes must equal the oracle's bit for bit, on rows built to hit the
 conversion's edge cases: all-zero blocks, ties between neighbouring E4M3
 values (to the even mantissa), block maxima whose scaled value lies above 448
@@ -98,6 +99,31 @@ def test_mx8_of_x_edge_cases():
         gh.torch_mod().cuda.synchronize()
         np.testing.assert_array_equal(gh.buf(g.layer, "x_q", np.uint8, (T, H)), want_c)
         np.testing.assert_array_equal(gh.buf(g.layer, "x_scale", np.uint8, (T, H // 32)), want_s)
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_quant_mx8_entry_edge_cases(src):
+    """moe_quant_mx8 on fp32 rows (fp32 subnormals, the byte clamped at 0) and
+    bf16 rows, with a ragged row count: codes and scales bit for bit."""
+    from mixture_experts_expert_moe_amd import moe
+    torch = gh.torch_mod()
+    rng = np.random.default_rng(91 if src == "f32" else 92)
+    rows, cols = 37, 768
+    v = rows_of(edge_blocks(rng, f32=(src == "f32")), cols, rows, rng)
+    if src == "bf16":
+        bits = bf16_bits_rne(v)
+        v = gh.bf16_to_f64(bits).astype(np.float32)
+        dev = torch.from_numpy(bits.view(np.int16)).to("cuda")
+    else:
+        dev = torch.from_numpy(v).to("cuda")
+    codes = torch.full((rows * cols,), 0x5a, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows * cols // 32,), 0x5a, dtype=torch.uint8, device="cuda")
+    say("moe_quant_mx8", src, rows, cols)
+    moe.moe_quant_mx8(rows, cols, src, dev, codes, scales)
+    torch.cuda.synchronize()
+    want_c, want_s, _ = oracle.quant_mx8(v)
+    np.testing.assert_array_equal(codes.cpu().numpy().reshape(rows, cols), want_c)
+    np.testing.assert_array_equal(scales.cpu().numpy().reshape(rows, cols // 32), want_s)
 
 
 def test_mx8_of_h_edge_cases():
