@@ -358,11 +358,18 @@ def mx4_figures(args, decode=True):
         wd, Ud, kd = rd.timed(args.steps, args.warmup)
         msd = wd / args.steps * 1e3
         b = gu_algorithmic_bytes(rd.spec, Td, Ud) + down_algorithmic_bytes(rd.spec, Td, Ud)
+        rd.fused = True  # the same layer through moe_decode_layer (one launch)
+        wf, Uf, kf = rd.timed(args.steps, args.warmup)
+        msf = wf / args.steps * 1e3
+        bl = b + 2 * rd.spec.n_routed * rd.spec.hidden  # + the router weights
         sweep[str(Td)] = {
             "tokens_per_s": round(Td / (msd / 1e3), 1), "ms_per_step": round(msd, 5),
             "kernel_ms": {k: round(v, 5) for k, v in kd.items()}, "touched_groups": Ud,
             "gemm_hbm_frac": round(b / ((kd["gate_up"] + kd["down"]) / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "gemm_algorithmic_bytes": b,
+            "one_launch": {"tokens_per_s": round(Td / (msf / 1e3), 1), "ms_per_step": round(msf, 5),
+                           "launch_ms": round(kf["decode_layer"], 5),
+                           "layer_hbm_frac": round(bl / (kf["decode_layer"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         }
         del rd
         torch.cuda.empty_cache()

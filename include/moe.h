@@ -256,10 +256,10 @@ moe_status moe_combine(const moe_desc* desc, int32_t T, const float* residual, v
  * topk_w, expert_offsets, row_token, token_row, sched, x_q, x_scale, h, h_q,
  * h_scale, y) holds the same bits as after those calls.
  *   w_router: [E][H] bf16;  bias: [E] fp32 or NULL
- *   w_gu, w_down: as for the GEMM calls (BF16, I8 or Q4B32 weights)
+ *   w_gu, w_down: as for the GEMM calls (BF16, I8, Q4B32 or MXFP4 weights)
  *   residual: [T][H] fp32 or NULL
  * Limits (else MOE_ERR_UNSUPPORTED): T * hidden <= 32768, inter <= 512,
- * hidden <= 8192, weights BF16, I8 or Q4B32. */
+ * hidden <= 8192, weights BF16, I8, Q4B32 or MXFP4. */
 #define MOE_DECODE_NORM_INPUT 1
 moe_status moe_decode_layer(const moe_desc* desc, int32_t T, const void* x, const void* w_router, const float* bias,
                             const moe_weights* w_gu, const moe_weights* w_down, const float* residual,

@@ -14,9 +14,9 @@
 // layer is one launch of one block per CU, with three grid-wide barriers:
 //
 //   P0  every block stages the layer input of every token in its LDS (the
-//       RMSNorm of the residual stream, or a copy of x) and, for int8
-//       weights, its int8 codes; then fp64 partial router logits of
-//       (expert, slice of H) units
+//       RMSNorm of the residual stream, or a copy of x) and, for int8 or
+//       MXFP4 weights, its int8 or MXFP8 codes; then fp64 partial router
+//       logits of (expert, slice of H) units
 //   --- barrier
 //   P1  every block sums the partials, takes the top-k of every token and
 //       builds the permutation and tile list in its own LDS (identical in
@@ -25,7 +25,8 @@
 //   P2  gate/up + SwiGLU: (tile, 16-pair) items, two per block at a time
 //   --- barrier (the first down round's weights are loaded while waiting)
 //   P3  down: (tile, 64-column) items, four per block at a time; each item
-//       stages its tile's h rows in LDS (int8: quantised per row there)
+//       stages its tile's h rows in LDS (int8: quantised per row there; MX:
+//       to MXFP8 per 32 columns)
 //   --- barrier
 //   P4  combine (+ residual): (token, 256-column) units spread over blocks
 //
@@ -171,7 +172,7 @@ constexpr int kMaxRows = kDecodeMaxT * 17;  // T * (k + S) with k <= 16, S <= 1
 constexpr int kSchedInts = kSchedHeader + 4 * kMaxGroups;
 template <int WF>
 struct Lds {
-  static constexpr bool kI8In = WF == kI8;
+  static constexpr bool kI8In = WF == kI8 || WF == kMX4;  // one-byte codes as the gate/up operand
   int32_t ids[kDecodeMaxT * 16];
   float gate[kDecodeMaxT * 16];
   int32_t off[kMaxGroups + 1];
@@ -179,6 +180,7 @@ struct Lds {
   int32_t token_row[kMaxRows];
   int32_t sched[kSchedInts];
   float x_scale[kDecodeMaxT];
+  alignas(16) uint8_t x_sc[WF == kMX4 ? kDecodeMaxTH / 32 : 16];  // MX: E8M0 bytes of the codes
   float part[8];
   alignas(16) int8_t act[kI8In ? kDecodeMaxTH : 2 * kDecodeMaxTH];  // int8 codes, or bf16 rows
   union alignas(16) {
@@ -194,8 +196,9 @@ struct Lds {
     } route;
     f32x4 red_gu[2 * 3 * 2 * kWave];  // 2 items x 3 waves x 2 blocks
     struct {
-      alignas(16) uint8_t h[4][16 * kDecodeMaxI * 2];  // 4 items x 16 rows (bf16, or int8 codes)
+      alignas(16) uint8_t h[4][16 * kDecodeMaxI * 2];  // 4 items x 16 rows (bf16, or int8 / E4M3 codes)
       float h_scale[4][16];
+      alignas(16) uint8_t h_sc[4][WF == kMX4 ? 16 * kDecodeMaxI / 32 : 16];  // MX: E8M0 bytes of the staged rows
       f32x4 red[4 * 4 * kWave];  // 4 items x 1 wave x 4 blocks
     } dn;
   } u;
@@ -205,7 +208,7 @@ struct Lds {
 template <int WF, bool kNormIn>
 __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
   __shared__ Lds<WF> L;
-  constexpr bool kF32Out = WF == kI8;  // h and y are fp32 for int8 weights, bf16 otherwise
+  constexpr bool kF32Out = WF == kI8 || WF == kMX4;  // h and y are fp32 for int8 and MX weights, else bf16
   const int T = a.T, H = a.H, I = a.I, E = a.E, k = a.k, S = a.S, G = E + S, kS = k + S;
   const int NB = gridDim.x, per_xcd = NB / kXcds;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
@@ -349,11 +352,45 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
         __syncthreads();  // s_max is reused by the next tokens
       }
     }
-    if constexpr (WF == kI8) {
+    if constexpr (WF == kMX4) {
+      // MXFP8 of every token (the conversion of moe_quant_mx8): a thread
+      // takes 8 consecutive values, the 4 threads of a 32-value block
+      // exchange their maxima (T * H / 8 is a multiple of the block size)
+      for (int i0 = 0; i0 < T * H / 8; i0 += kThreads) {
+        const int i = i0 + tid;
+        float v[8];
+        if (i < T * H / 8) bf16x8_to_f32(*reinterpret_cast<const u32x4*>(xin + 8 * i), v);
+        else
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = 0.f;
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(v[j]));
+        m = fmaxf(m, __shfl_xor(m, 1));
+        m = fmaxf(m, __shfl_xor(m, 2));
+        const uint32_t sb = mx8_scale_byte(m);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          lo |= e4m3_code(v[j], sb) << (8 * j);
+          hi |= e4m3_code(v[4 + j], sb) << (8 * j);
+        }
+        if (i < T * H / 8) {
+          *reinterpret_cast<u32x2*>(L.act + 8 * i) = u32x2{lo, hi};
+          if ((i & 3) == 0) L.x_sc[i / 4] = (uint8_t)sb;
+        }
+      }
+      __syncthreads();
+    }
+    if constexpr (WF == kI8 || WF == kMX4) {
       if (lead) {
         for (int i = tid; i < T * H / 8; i += kThreads)
           reinterpret_cast<u32x2*>(a.x_q)[i] = reinterpret_cast<const u32x2*>(L.act)[i];
-        if (tid < T) a.x_scale[tid] = L.x_scale[tid];
+        if constexpr (WF == kI8) {
+          if (tid < T) a.x_scale[tid] = L.x_scale[tid];
+        } else {
+          for (int i = tid; i < T * H / 32; i += kThreads) reinterpret_cast<uint8_t*>(a.x_scale)[i] = L.x_sc[i];
+        }
       }
     }
     grid_wait(a.sync, g0, a.spin_ns);
@@ -426,7 +463,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
     Kp p{};
     p.act = xin;
     p.act_q = L.act;
-    p.act_scale = L.x_scale;
+    p.act_scale = WF == kMX4 ? reinterpret_cast<const float*>(L.x_sc) : L.x_scale;
     p.row_token = L.row_token;
     p.w = a.w_gu;
     p.w_scale = a.gu_scale;
@@ -473,12 +510,12 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
     p.R = R;
     p.act = L.u.dn.h[quarter];
     p.act_q = reinterpret_cast<const int8_t*>(L.u.dn.h[quarter]);
-    p.act_scale = L.u.dn.h_scale[quarter];
+    p.act_scale = WF == kMX4 ? reinterpret_cast<const float*>(L.u.dn.h_sc[quarter]) : L.u.dn.h_scale[quarter];
     Acc<WF>* red = reinterpret_cast<Acc<WF>*>(L.u.dn.red) + quarter * 4 * kWave;
     // I <= 512: a wave's share of K is one register batch (int8) or two, all
     // of them sent early except the second of bf16's (64 registers each)
     DownItem<WF, WF == kI8 ? 1 : 2, WF == kBF16 ? 1 : (WF == kI8 ? 1 : 2)> di;
-    const CohBuf hbuf(a.h, (uint32_t)(R * I * (WF == kI8 ? 4 : 2)));
+    const CohBuf hbuf(a.h, (uint32_t)(R * I * (kF32Out ? 4 : 2)));
     for (int base = 0; base < n_items; base += 4 * NB) {
       const int it = base + quarter * NB + (int)blockIdx.x;
       const bool act = it < n_items;
@@ -536,6 +573,39 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
             if (lane == 0) {
               L.u.dn.h_scale[quarter][r] = sc;
               if (n0 == 0) a.h_scale[row0 + r] = sc;
+            }
+          } else if constexpr (WF == kMX4) {
+            // MXFP8 per 32 columns: lane chunks of 4 values, the 8 lanes of
+            // a block exchange their maxima (I <= 512: j < 2; I % 256 == 0)
+            const uint32_t src = (uint32_t)((row0 + r) * I) * 4;
+            uint64_t v[2][2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int c = 4 * lane + 4 * kWave * j;
+              v[j][0] = hbuf.ld64(c < I ? src + 4 * c : kNoOffset);
+              v[j][1] = hbuf.ld64(c < I ? src + 4 * c + 8 : kNoOffset);
+            }
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+              const int c = 4 * lane + 4 * kWave * j;
+              float f[4] = {__uint_as_float((uint32_t)v[j][0]), __uint_as_float((uint32_t)(v[j][0] >> 32)),
+                            __uint_as_float((uint32_t)v[j][1]), __uint_as_float((uint32_t)(v[j][1] >> 32))};
+              float m = fmaxf(fmaxf(fabsf(f[0]), fabsf(f[1])), fmaxf(fabsf(f[2]), fabsf(f[3])));
+              m = fmaxf(m, __shfl_xor(m, 1));
+              m = fmaxf(m, __shfl_xor(m, 2));
+              m = fmaxf(m, __shfl_xor(m, 4));
+              const uint32_t sb = mx8_scale_byte(m);
+              const uint32_t b = e4m3_code(f[0], sb) | e4m3_code(f[1], sb) << 8 | e4m3_code(f[2], sb) << 16 |
+                                 e4m3_code(f[3], sb) << 24;
+              if (c < I) {
+                *reinterpret_cast<uint32_t*>(&L.u.dn.h[quarter][r * I + c]) = b;
+                if ((lane & 7) == 0) L.u.dn.h_sc[quarter][r * (I / 32) + c / 32] = (uint8_t)sb;
+                if (n0 == 0) {
+                  *reinterpret_cast<uint32_t*>(a.h_q + (size_t)(row0 + r) * I + c) = b;
+                  if ((lane & 7) == 0)
+                    reinterpret_cast<uint8_t*>(a.h_scale)[(size_t)(row0 + r) * (I / 32) + c / 32] = (uint8_t)sb;
+                }
+              }
             }
           } else {
             const uint32_t src = (uint32_t)((row0 + r) * I) * 2;
@@ -668,6 +738,7 @@ hipError_t launch_decode_layer(const DecodeArgs& a, hipStream_t stream) {
     case kBF16: launch_fmt<kBF16>(a, nb, stream); break;
     case kI8: launch_fmt<kI8>(a, nb, stream); break;
     case kQ4: launch_fmt<kQ4>(a, nb, stream); break;
+    case kMX4: launch_fmt<kMX4>(a, nb, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

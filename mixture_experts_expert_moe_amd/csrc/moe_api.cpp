@@ -337,7 +337,6 @@ moe_status moe_decode_layer(const moe_desc* d, int32_t T, const void* x, const v
   moe_status s = check_call(d, T, b);
   if (s != MOE_OK) return s;
   if ((s = check_weights(d, w_gu)) != MOE_OK || (s = check_weights(d, w_down)) != MOE_OK) return s;
-  const bool i8 = d->w_dtype == MOE_I8;
   const bool norm = (flags & MOE_DECODE_NORM_INPUT) != 0;
   if ((flags & ~MOE_DECODE_NORM_INPUT) != 0 || (norm && residual)) return MOE_ERR_INVALID_ARG;
   if (!ptr_ok(x) || !ptr_ok(w_router) || (bias && !aligned16(bias)) || !ptr_ok(out) ||
@@ -347,10 +346,9 @@ moe_status moe_decode_layer(const moe_desc* d, int32_t T, const void* x, const v
       !ptr_ok(b->row_token) || !ptr_ok(b->token_row) || !ptr_ok(b->sched) || !ptr_ok(b->h) || !ptr_ok(b->y) ||
       !ptr_ok(b->sync))
     return MOE_ERR_INVALID_ARG;
-  if (i8 && (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale) || !ptr_ok(b->h_q) || !ptr_ok(b->h_scale)))
+  if (quant_act(d) && (!ptr_ok(b->x_q) || !ptr_ok(b->x_scale) || !ptr_ok(b->h_q) || !ptr_ok(b->h_scale)))
     return MOE_ERR_INVALID_ARG;
-  if (d->act_dtype != MOE_BF16 || d->w_dtype == MOE_F32 || d->w_dtype == MOE_MXFP4 ||
-      (norm && d->out_dtype != MOE_F32))
+  if (d->act_dtype != MOE_BF16 || d->w_dtype == MOE_F32 || (norm && d->out_dtype != MOE_F32))
     return MOE_ERR_UNSUPPORTED;
   if (T > moe::kDecodeMaxT || (int64_t)T * d->hidden > moe::kDecodeMaxTH || d->inter > moe::kDecodeMaxI ||
       d->hidden > 8192)

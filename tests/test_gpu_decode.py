@@ -1,8 +1,8 @@
 """moe_decode_layer: the whole layer for a few tokens in one launch.
 
 It must write, bit for bit, what the separate calls write (routing,
-permutation, tile schedule, int8 codes, h, y and the output, also with the
-RMSNorm of the residual stream in front), match the oracle (routing
+permutation, tile schedule, int8 or MXFP8 codes, h, y and the output, also
+with the RMSNorm of the residual stream in front), match the oracle (routing
 exactly, outputs within the float bar, the int8 path exactly), leave the
 barrier status word clear, and give the same bits when called many times in
 a row and when replayed from a graph."""
@@ -38,6 +38,9 @@ CASES = [
     ("i8_e32k8_t7_noshared", 1024, 256, 32, 8, 0, 7, "i8"),
     ("q4_e256k16s1_t16_h1024", 1024, 512, 256, 16, 1, 16, "q4"),
     ("bf16_e8k8s1_t9_h256", 256, 256, 8, 8, 1, 9, "bf16"),
+    ("mx4_e128k8s1_t1", 2048, 512, 128, 8, 1, 1, "mx4"),
+    ("mx4_e128k8s1_t8", 2048, 512, 128, 8, 1, 8, "mx4"),
+    ("mx4_e32k8_t11_noshared_i256", 1024, 256, 32, 8, 0, 11, "mx4"),
 ]
 
 BUFS = ("logits", "topk_ids", "topk_w", "expert_offsets", "row_token", "token_row", "x_q", "x_scale", "h", "y",
@@ -54,10 +57,12 @@ def case_inputs(H, I, E, k, S, T, wt, seed):
 
 def nbytes(spec, T):
     R = T * (spec.top_k + spec.n_shared)
-    f = 4 if spec.wt == "i8" else 2
+    f = 4 if spec.wt in ("i8", "mx4") else 2
+    mx = spec.wt == "mx4"
     return dict(logits=T * spec.n_routed * 4, topk_ids=T * spec.top_k * 4, topk_w=T * spec.top_k * 4,
                 expert_offsets=(spec.groups + 1) * 4, row_token=R * 4, token_row=R * 4, x_q=T * spec.hidden,
-                x_scale=T * 4, h=R * spec.inter * f, y=R * spec.hidden * f, h_q=R * spec.inter, h_scale=R * 4)
+                x_scale=T * spec.hidden // 32 if mx else T * 4, h=R * spec.inter * f, y=R * spec.hidden * f,
+                h_q=R * spec.inter, h_scale=R * spec.inter // 32 if mx else R * 4)
 
 
 def snapshot(g, spec, T):
@@ -118,7 +123,7 @@ def test_decode_layer_equals_separate_calls_and_oracle(case):
     say("  ok: max_rel %.3g rmse %.3g" % (mr, rm))
 
 
-@pytest.mark.parametrize("wt,T", [("q4", 1), ("i8", 8), ("bf16", 3), ("q4", 16)])
+@pytest.mark.parametrize("wt,T", [("q4", 1), ("i8", 8), ("bf16", 3), ("q4", 16), ("mx4", 4)])
 def test_decode_layer_norm_input_and_repeats(wt, T):
     """With the RMSNorm of the fp32 residual stream inside (one stacked layer):
     the same bits as moe_rmsnorm + the separate calls with the residual, in

@@ -152,17 +152,3 @@ def test_mx8_of_h_edge_cases():
     offsets = g.offsets()
     y_ref = oracle.down(h.astype(np.float64), offsets, H, "mx4", d["w_down"], d["w_down_scale"], None)
     gh.assert_within(g.y(), y_ref, gh.mx_down_bound(d, offsets, h, y_ref), what="down of the edge-case h")
-
-
-def test_mx_rejected_by_decode_layer():
-    """The one-launch decode layer does not take MXFP4 weights: it says so before any launch."""
-    from mixture_experts_expert_moe_amd import moe
-    spec = LayerSpec(hidden=512, inter=256, n_routed=16, top_k=4, n_shared=1, act="bf16", wt="mx4", out="f32")
-    d = synth.layer_weights(spec, 8300)
-    d["x"] = synth.tokens(spec, 8300, 2)
-    d["spec"] = spec
-    g = gh.GpuLayer(d, max_tokens=4)
-    out = gh.torch_mod().zeros((2, 512), dtype=gh.torch_mod().float32, device="cuda")
-    with pytest.raises(moe.MoeError) as e:
-        g.layer.forward_decode(g.x, out)
-    assert e.value.status == -2

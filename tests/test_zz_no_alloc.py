@@ -18,7 +18,7 @@ def say(*a):
     sys.stdout.flush()
 
 
-@pytest.mark.parametrize("wt,norm", [("i8", False), ("q4", True), ("bf16", False)])
+@pytest.mark.parametrize("wt,norm", [("i8", False), ("q4", True), ("bf16", False), ("mx4", True)])
 def test_static_variant_equals_buffered_call(wt, norm):
     torch = gh.torch_mod()
     from mixture_experts_expert_moe_amd import moe
