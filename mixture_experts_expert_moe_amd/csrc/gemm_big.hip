@@ -627,8 +627,7 @@ void big_gemm_kernel(Bp p) {
 template <bool kGU>
 hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (a.wfmt != kBF16 && a.wfmt != kQ4 && a.wfmt != kMX4) return hipErrorInvalidValue;
-  // bf16 small tiles keep the K-split kernel; 4-bit and MX small tiles always run here
-  if (with_small != (a.wfmt != kBF16)) return hipErrorInvalidValue;
+  if (!with_small) return hipErrorInvalidValue;  // the small tiles always run in the same launch
   const int cols = kGU ? kBN / 2 : kBN;
   if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
   const bool mx = a.wfmt == kMX4;
@@ -644,10 +643,10 @@ hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   if (mx)
     hipLaunchKernelGGL((big_gemm_kernel<kMX4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
-  else if (with_small)
+  else if (a.wfmt == kQ4)
     hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
   else
-    hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU, false>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -55,7 +55,6 @@ struct GemmArgs {
   int K;                    // reduction length (H for gate/up, I for down)
   int N;                    // output columns (I for gate/up, H for down)
   int wfmt;                 // WFmt (also fixes the activation/output formats, see moe.h)
-  bool big_on;              // the schedule has big tiles (launch the big-tile kernel too)
   int T;                    // tokens (gate/up clamps row_token into [0, T))
   int R;                    // permuted rows, T * (k + S)
   int G;                    // groups

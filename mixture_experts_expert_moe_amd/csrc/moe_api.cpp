@@ -91,11 +91,9 @@ bool big_tiles(const moe_desc* d, int32_t T) {
          (d->w_dtype == MOE_MXFP4 && mx_offsets_fit(d));
 }
 
-// With big tiles on, the small tiles of 4-bit and MX weights go through the
-// big-tile kernel too, in the same launch as the big tiles.
-bool q4_small_reg(const moe_desc* d, int32_t T) {
-  return (d->w_dtype == MOE_Q4B32 || d->w_dtype == MOE_MXFP4) && big_tiles(d, T);
-}
+// With big tiles on, the small tiles go through the big-tile kernel too, in
+// the same launch as the big tiles (one launch per GEMM at every T).
+bool small_in_big(const moe_desc* d, int32_t T) { return big_tiles(d, T); }
 
 moe_status check_weights(const moe_desc* d, const moe_weights* w) {
   if (!w || !ptr_ok(w->w)) return MOE_ERR_INVALID_ARG;
@@ -250,12 +248,7 @@ moe_status moe_grouped_gemm_gu(const moe_desc* d, int32_t T, const void* x, cons
   a.T = T;
   a.R = (int)rows(d, T);
   a.G = groups(d);
-  a.big_on = big_tiles(d, T);
-  if (q4_small_reg(d, T)) return hip_status(moe::launch_big_gate_up(a, true, stream));
-  if (a.big_on) {
-    const hipError_t e = moe::launch_big_gate_up(a, false, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-  }
+  if (small_in_big(d, T)) return hip_status(moe::launch_big_gate_up(a, true, stream));
   return hip_status(moe::launch_gate_up(a, stream));
 }
 
@@ -295,12 +288,7 @@ moe_status moe_grouped_gemm_down(const moe_desc* d, int32_t T, const moe_weights
   a.T = T;
   a.R = R;
   a.G = groups(d);
-  a.big_on = big_tiles(d, T);
-  if (q4_small_reg(d, T)) return hip_status(moe::launch_big_down(a, true, stream));
-  if (a.big_on) {
-    const hipError_t e = moe::launch_big_down(a, false, stream);
-    if (e != hipSuccess) return MOE_ERR_HIP;
-  }
+  if (small_in_big(d, T)) return hip_status(moe::launch_big_down(a, true, stream));
   return hip_status(moe::launch_down(a, stream));
 }
 
