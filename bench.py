@@ -389,7 +389,7 @@ def main():
     ap.add_argument("--no-fp32", action="store_true", help="skip the fp32 16-expert figure")
     ap.add_argument("--no-stack", action="store_true", help="skip the 40-layer 4-bit stack figures")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens of the workload the oracle runs")
-    ap.add_argument("--workloads", default="headline,decode,fp32,q4,mx4,stack",
+    ap.add_argument("--workloads", default="headline,decode,fp32,q4,q4c,mx4,stack",
                     help="comma list of the parts to run (profiling runs pick one; mx4p: the MX prefill only); "
                          "without 'headline' the line's value is null")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -509,6 +509,24 @@ def main():
                                     / MFMA_BF16_PEAK_TFLOPS, 4),
         }
         del rq
+        torch.cuda.empty_cache()
+
+    if "q4c" in parts:
+        # one layer of the 4-bit stack at its prefill chunk (T = 256, uniform
+        # routing): HBM-bound, every group's weights read once per launch
+        Tc = 256
+        rc = Runner("q4_stack40", Tc, args.rotations, args.steps + args.warmup)
+        wc, Uc, kc = rc.timed(args.steps, args.warmup)
+        msc = wc / args.steps * 1e3
+        bg, bd = gu_algorithmic_bytes(rc.spec, Tc, Uc), down_algorithmic_bytes(rc.spec, Tc, Uc)
+        extra["prefill_q4_chunk_t256"] = {
+            "tokens_per_s": round(Tc / (msc / 1e3), 1), "ms_per_step": round(msc, 5),
+            "kernel_ms": {k: round(v, 5) for k, v in kc.items()}, "touched_groups": Uc,
+            "gate_up_hbm_frac": round(bg / (kc["gate_up"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "down_hbm_frac": round(bd / (kc["down"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "gemm_algorithmic_bytes": bg + bd,
+        }
+        del rc
         torch.cuda.empty_cache()
 
     if "mx4" in parts or "mx4p" in parts:

@@ -58,15 +58,24 @@ constexpr int kSK = 128;                 // K per super-stage
 // register file and two blocks share a CU, each covering the other's load
 // latency, prologue and epilogue.
 #ifndef MOE_BIG_RING_Q4
-#define MOE_BIG_RING_Q4 2
+#define MOE_BIG_RING_Q4 3
 #endif
 #ifndef MOE_BIG_RING_MX
 #define MOE_BIG_RING_MX 4
 #endif
-template <int WF>
-constexpr int ring() { return WF == kQ4 ? MOE_BIG_RING_Q4 : WF == kMX4 ? MOE_BIG_RING_MX : 3; }
-static_assert(MOE_BIG_RING_Q4 == 2 || MOE_BIG_RING_Q4 == 3, "ring depth");
+// 4-bit items of at most 32 token rows (short tiles) do a sixteenth or an
+// eighth of a 128-row item's MFMAs per weight byte: the registers of their
+// accumulators go to a deeper ring.
+#ifndef MOE_BIG_RING_SHORT
+#define MOE_BIG_RING_SHORT 4
+#endif
+template <int WF, int BM>
+constexpr int ring() {
+  return WF == kQ4 ? (BM <= 32 ? MOE_BIG_RING_SHORT : MOE_BIG_RING_Q4) : WF == kMX4 ? MOE_BIG_RING_MX : 3;
+}
+static_assert(MOE_BIG_RING_Q4 == 3, "ring depth: three 32 KB token stages and the item's scales fill the LDS");
 static_assert(MOE_BIG_RING_MX >= 3 && MOE_BIG_RING_MX <= 4, "ring depth");
+static_assert(MOE_BIG_RING_SHORT >= 2 && MOE_BIG_RING_SHORT <= 4, "ring depth");
 constexpr int kThreads = 256;
 // Token rows per block: kBigTileRows for the big-tile list, kTileRows for the
 // small-tile list.  Bytes of one token row per super-stage (bf16: 256, E4M3:
@@ -88,6 +97,12 @@ template <int WF, int BM> constexpr int b_stage_bytes() { return b_data_bytes<WF
 // the last chunk repeat it into the padding).
 constexpr int kMxMaxK = 2048;
 constexpr int kMxScaleBytes = kBN * (kMxMaxK / 32) + kBigTileRows * (kMxMaxK / 32);
+// 4-bit item scales and mins in LDS (K <= kQ4MaxK, K % 256 == 0): the 256
+// weight rows' fp16 scales, then their fp16 mins, K / 32 of each per row; the
+// 16-byte DMA chunks of one array are K per item, K / 256 instructions per wave.
+constexpr int kQ4MaxK = 2048;
+constexpr int kQ4ArrayBytes = kBN * (kQ4MaxK / 32) * 2;
+constexpr int kQ4ScaleBytes = 2 * kQ4ArrayBytes;
 __device__ __forceinline__ int mx_a_dma(int K) { return K / 512; }
 template <int BM> __device__ __forceinline__ int mx_b_dma(int K) { return max(1, BM * (K / 512) / 256); }
 template <int WF, int BM> constexpr int b_dma_per_wave() { return b_data_bytes<WF, BM>() / 1024 / 4; }
@@ -98,6 +113,12 @@ template <int WF> __device__ __forceinline__ int b_swz(int row) {
   return WF == kMX4 ? (row >> 1) & 7 : row % 16;
 }
 static_assert(kBigTileRows == 128 && kTileRows == 64, "tile heights the B loader and fragments are laid out for");
+// Item heights: 128 (big tiles), 64, 32 and 16 (small tiles, by their rows;
+// MX: 32 at least, one 1 KB DMA of token rows per wave).
+template <int WF, int BM>
+constexpr bool item_height_ok() {
+  return (BM == 128 || BM == 64 || BM == 32 || (BM == 16 && WF != kMX4)) && b_dma_per_wave<WF, BM>() >= 1;
+}
 
 struct Bp {
   const void* act;          // x [T][K] (gate/up, gathered by row_token) or h [R][K] (down), bf16 (MX: E4M3)
@@ -121,70 +142,42 @@ __device__ __forceinline__ u32x4 gload16(const void* p) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
   return r;
 }
-__device__ __forceinline__ uint32_t gload_u16(const void* p) {
-  uint32_t r;
-  asm volatile("global_load_ushort %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
 // Same loads at a 32-bit byte offset from a uniform base (scalar base + vector offset).
 __device__ __forceinline__ u32x4 gload16(const void* base, uint32_t off) {
   u32x4 r;
   asm volatile("global_load_dwordx4 %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
   return r;
 }
-__device__ __forceinline__ uint32_t gload_u16(const void* base, uint32_t off) {
-  uint32_t r;
-  asm volatile("global_load_ushort %0, %1, %2" : "=v"(r) : "v"(off), "s"(base) : "memory");
-  return r;
-}
 
 
-// Vector-memory loads each thread issues per super-stage (LDS DMA + A; MX:
-// + one DMA of token scale bytes).
+// Vector-memory loads each thread issues per super-stage (LDS DMA + A).
 template <int WF, int BM>
 constexpr int loads_per_stage() {
-  return b_dma_per_wave<WF, BM>() + (WF == kQ4 ? 4 + 8 : WF == kMX4 ? 4 : 16);
+  return b_dma_per_wave<WF, BM>() + (WF == kQ4 || WF == kMX4 ? 4 : 16);
 }
 
 // One wave's A operand for one super-stage: 4 fragments of 16 weight rows.
 //   4-bit: lane (r, q) holds the 16 bytes of block q of the super-stage
-//          (codes k = 32q .. 32q+31) and that block's scale and min;
+//          (codes k = 32q .. 32q+31); the scales and mins are in LDS;
 //   bf16:  lane (r, q) holds, for step kk, elements k = 32kk + 8q .. +7.
 //   MX:    lane (r, q) holds the 16 bytes of block q (elements k = 32q .. 32q+31);
 //          the scale bytes are in LDS.
 template <int WF>
 struct ATile {
   u32x4 v[4][WF == kQ4 || WF == kMX4 ? 1 : 4];
-  uint32_t sc[4], mn[4];  // 4-bit only: fp16 bits
 };
 
 // Part g (0..7) of one super-stage's A loads (the loads are spread over the
-// eight MFMA groups of the previous super-stage).  4-bit: group g loads the
-// scale (g even) or min (g odd) of fragment g / 2, and the codes of fragment
-// g / 2 on even g; bf16: fragment g / 2, steps 2 (g % 2) and 2 (g % 2) + 1.
+// eight MFMA groups of the previous super-stage).  4-bit and MX: the codes of
+// fragment g / 2 on even g; bf16: fragment g / 2, steps 2 (g % 2) and
+// 2 (g % 2) + 1.
 template <int WF, class Row>
 __device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row (&arow)[4], int S, int q, int g) {
   const int b = g / 2;
-  if constexpr (WF == kMX4) {
-    static_assert(sizeof(Row) == 4, "MX weights use 32-bit offsets");
-    if (g % 2 == 0) a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
-  } else if constexpr (WF == kQ4 && sizeof(Row) == 4) {
+  if constexpr (WF == kMX4 || WF == kQ4) {
     // 32-bit offsets (the launcher checks that the weights fit)
-    const uint32_t blk2 = 2u * (arow[b] * (uint32_t)(p.K / 32) + S * (kSK / 32) + q);
-    if (g % 2 == 0) {
-      a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
-      a.sc[b] = gload_u16(p.w_scale, blk2);
-    } else {
-      a.mn[b] = gload_u16(p.w_min, blk2);
-    }
-  } else if constexpr (WF == kQ4) {
-    const size_t blk = arow[b] * (size_t)(p.K / 32) + S * (kSK / 32) + q;
-    if (g % 2 == 0) {
-      a.v[b][0] = gload16((const uint8_t*)p.w + arow[b] * (size_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
-      a.sc[b] = gload_u16((const uint16_t*)p.w_scale + blk);
-    } else {
-      a.mn[b] = gload_u16((const uint16_t*)p.w_min + blk);
-    }
+    static_assert(sizeof(Row) == 4, "4-bit and MX weights use 32-bit offsets");
+    if (g % 2 == 0) a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
   } else {
 #pragma unroll
     for (int kk = 2 * (g % 2); kk < 2 * (g % 2) + 2; ++kk)
@@ -199,7 +192,6 @@ __device__ __forceinline__ void tie(ATile<WF>& a) {
   for (int b = 0; b < 4; ++b) {
 #pragma unroll
     for (int i = 0; i < (WF == kQ4 || WF == kMX4 ? 1 : 4); ++i) asm volatile("" : "+v"(a.v[b][i]));
-    if constexpr (WF == kQ4) asm volatile("" : "+v"(a.sc[b]), "+v"(a.mn[b]));
   }
 }
 
@@ -263,26 +255,28 @@ __device__ __forceinline__ u32x4 a_frag(const ATile<WF>& a, const Q4Block (&qs)[
 // loads of a later super-stage (issue_part(p)) are spread evenly over the
 // groups, so that the memory pipeline fills while the MFMAs run instead of in
 // one burst.  sched_barrier pins that order.
-// MX scale bytes of one super-stage in LDS: a[b] = this lane's byte for
+// Item scales of one super-stage in LDS.  MX: a[b] = this lane's byte for
 // weight fragment b (its row, block 4 S + q), b = token block 0's (row lr),
-// token block c's at b + c * bstep.
-struct MxSc {
+// token block c's at b + c * bstep.  4-bit: s[b], m[b] = the fp16 bits of
+// the scale and min of weight fragment b's block 4 S + q (read from LDS one
+// super-stage ahead).
+struct ItemSc {
   const uint8_t* a[4];
   const uint8_t* b;
   int bstep;
+  uint32_t s[4], m[4];
 };
 
 template <int WF, int BM, class IssuePart>
 __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[4][BM / 16], int lr,
-                                        int q, IssuePart&& issue_part, const MxSc& sc = MxSc{}) {
-  constexpr int NG = BM / 64, G = 4 * NG, PPG = 8 / G;  // groups per step, groups, load parts per group
-  constexpr bool kLean = ring<WF>() == 2;
+                                        int q, IssuePart&& issue_part, const ItemSc& sc = ItemSc{}) {
+  constexpr int NG = BM / 64, G = 4 * NG, PPG = G > 0 ? 8 / G : 0;  // groups per step, groups, load parts per group
   if constexpr (WF == kMX4) {
     // One scaled MFMA per (weight block, token block), in groups of GW token
     // blocks; the next group's two FP8 halves and scale bytes are read from
     // LDS before the current group's 4 GW MFMAs are issued (one wave per
     // SIMD: nothing else would cover the LDS latency).
-    constexpr int GW = 4, MG = BM / 16 / GW, MPPG = 8 / MG;
+    constexpr int GW = BM / 16 < 4 ? BM / 16 : 4, MG = BM / 16 / GW, MPPG = 8 / MG;
     // Row 16c + lr of the stage: the swizzle depends on lr alone, so the LDS
     // addresses of a token block differ from block 0's by a constant.
     const uint8_t* h0 = st + lr * b_row_bytes<WF>() + 16 * (b_chunk<WF>(q, 0) ^ b_swz<WF>(lr));
@@ -325,7 +319,81 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
   Q4Block qs[4];
   if constexpr (WF == kQ4) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) qs[b] = q4_block(a.sc[b], a.mn[b]);
+    for (int b = 0; b < 4; ++b) qs[b] = q4_block(sc.s[b], sc.m[b]);
+    // 4-bit, every item height, one wave per SIMD: while the 4 NC MFMAs of
+    // step kk run, the same wave decodes the weight fragments of step kk + 1
+    // and reads its token fragments from LDS, so the decode (about two VALU
+    // instructions per weight) and the LDS latency hide under the matrix pipe
+    // (or, for short items, the MFMAs under the decode).  sched_group_barrier
+    // pins the interleave: the LDS reads, then one MFMA and a share of the
+    // decode at a time.
+    constexpr int NC = BM / 16, NM = 4 * NC, VPM = (96 + NM - 1) / NM;
+    auto bfr = [&](int kk, int c) {
+      return *reinterpret_cast<const u32x4*>(st + (16 * c + lr) * (kSK * 2) + 16 * (b_chunk<WF>(q, kk) ^ lr));
+    };
+    u32x4 af[4], bf[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) bf[c] = bfr(0, c);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, 0);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_part(2 * kk);
+      issue_part(2 * kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4 an[4], bn[NC];
+      if (kk < 3) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) bn[c] = bfr(kk + 1, c);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) an[b] = a_frag<WF>(a, qs, b, kk + 1);
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[b][c] = mfma_bf16_16x16x32(af[b], bf[c], acc[b][c]);
+      if (kk < 3) {
+        __builtin_amdgcn_sched_group_barrier(0x100, NC, 0);  // LDS reads
+#pragma unroll
+        for (int i = 0; i < NM; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // a share of the decode
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 3) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) bf[c] = bn[c];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) af[b] = an[b];
+      }
+    }
+    return;
+  }
+  if constexpr (BM < 64) {
+    // Short bf16 items (one or two token blocks): per step kk, two parts of
+    // the later loads, the NC token fragments, the four weight fragments and
+    // 4 NC MFMAs.
+    constexpr int NC = BM / 16;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_part(2 * kk);
+      issue_part(2 * kk + 1);
+      u32x4 af[4], bf[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        bf[c] = *reinterpret_cast<const u32x4*>(st + (16 * c + lr) * (kSK * 2) + 16 * (b_chunk<WF>(q, kk) ^ lr));
+#pragma unroll
+      for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, kk);
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[b][c] = mfma_bf16_16x16x32(af[b], bf[c], acc[b][c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return;
   }
 
   // token row 16c + lr, chunk slot b_chunk ^ lr (the row's low 4 bits are lr)
@@ -333,31 +401,6 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
     return *reinterpret_cast<const u32x4*>(st + (16 * c + lr) * (kSK * 2) + 16 * (b_chunk<WF>(q, kk) ^ lr));
   };
   u32x4 af[4], bf[4];
-  if constexpr (kLean) {
-    // Two waves per SIMD: no operand prefetch (the other wave's MFMAs cover
-    // the LDS latency and the decode), so that the registers go to occupancy:
-    // per group, the token fragments are read and (first group of a step) the
-    // weight fragments decoded right before the 16 MFMAs that use them.
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int kk = g / NG, c0 = 4 * (g % NG);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int pp = 0; pp < PPG; ++pp) issue_part(g * PPG + pp);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) bf[i] = bfrag(kk, c0 + i);
-      if (g % NG == 0) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, kk);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[b][c0 + i] = mfma_bf16_16x16x32(af[b], bf[i], acc[b][c0 + i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    return;
-  }
 #pragma unroll
   for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, 0);
 #pragma unroll
@@ -407,8 +450,10 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   const int wave = __builtin_amdgcn_readfirstlane(t / kWave);  // uniform: keep it in a scalar register
   const int lr = lane % 16, q = lane / 16;
 
-  constexpr int kRing = ring<WF>(), kAhead = kRing - 1;
-  constexpr bool k32 = kRing == 2 || WF == kMX4;  // 32-bit offsets
+  static_assert(item_height_ok<WF, BM>(), "item height");
+  constexpr int kRing = ring<WF, BM>(), kAhead = kRing - 1;
+  static_assert(kRing * kBStage <= ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>(), "ring fits the LDS");
+  constexpr bool k32 = WF == kQ4 || WF == kMX4;  // 32-bit offsets
   using Row = typename std::conditional<k32, uint32_t, size_t>::type;
   using Src = typename std::conditional<k32, uint32_t, const uint8_t*>::type;
   // A rows of this wave's 4 fragments (GU: gate cols i0.., i0+16.., then the up rows).
@@ -440,7 +485,7 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   // MX: the item's scale bytes -> LDS after the ring (weight rows, then token
   // rows; K / 32 bytes per row, 16-byte chunks, lane-consecutive), issued
   // before the first super-stage's loads, so the first wait covers them.
-  uint8_t* const asc_lds = lds + kRing * b_stage_bytes<WF, kBigTileRows>();
+  uint8_t* const asc_lds = lds + ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>();
   uint8_t* const bsc_lds = asc_lds + kBN * (kMxMaxK / 32);
   const int kpr = p.K / 32;
   if constexpr (WF == kMX4) {
@@ -467,16 +512,49 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
       }
     }
   }
-  // MX: this lane's scale bytes of super-stage S (block 4 S + q): weight
-  // fragment b's row, token block 0's row (lr); token block c at + 16 c kpr.
-  auto mx_sc = [&](int S) {
-    MxSc sc{};
-    if constexpr (WF == kMX4) {
+  // 4-bit: the item's fp16 scales and mins -> LDS after the ring (the 256
+  // weight rows in item order, K / 32 values per row; 16-byte chunks,
+  // lane-consecutive), issued before the first super-stage's loads, so the
+  // first wait covers them.  Read per super-stage from global memory instead,
+  // each row's 128-byte lines of scales and mins were touched once per
+  // super-stage over the whole item and fell out of L2 in between.  The
+  // chunks of a row sit XOR-swizzled by the row (when the chunks per row are
+  // a power of two), so that the 16 rows of a fragment read one block's
+  // values from different banks.
+  uint16_t* const qsc_lds = reinterpret_cast<uint16_t*>(lds + ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>());
+  uint16_t* const qmn_lds = qsc_lds + kQ4ArrayBytes / 2;
+  if constexpr (WF == kQ4) {
+    const int cpr = p.K / 256, n = p.K / 256;  // chunks per row; instructions per wave and array
+    const int sw = (cpr & (cpr - 1)) == 0 ? cpr - 1 : 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int lw = kGU ? (b < 2 ? 0 : 128) + 32 * wave + 16 * (b & 1) + lr : 64 * wave + 16 * b + lr;
-        sc.a[b] = asc_lds + lw * kpr + 4 * S + q;
+    for (int i = 0; i < kQ4MaxK / 256; ++i) {
+      if (i < n) {
+        const int ci = (wave * n + i) * kWave + lane;  // < 256 cpr
+        const int lw = ci / cpr, part = (ci % cpr) ^ (lw & sw);
+        const uint32_t grow = kGU ? (uint32_t)group * 2 * p.N + (lw < 128 ? n0 + lw : p.N + n0 + lw - 128)
+                                  : (uint32_t)group * p.N + n0 + lw;
+        const uint32_t off = grow * (uint32_t)(kpr * 2) + 16 * part;
+        load_scale_chunk((uint8_t*)qsc_lds + (wave * n + i) * 1024, (const uint8_t*)p.w_scale + off);
+        load_scale_chunk((uint8_t*)qmn_lds + (wave * n + i) * 1024, (const uint8_t*)p.w_min + off);
       }
+    }
+  }
+  // This lane's item scales of super-stage S (block 4 S + q): weight fragment
+  // b's row; MX also token block 0's row (lr), token block c at + 16 c kpr.
+  auto item_sc = [&](int S) {
+    ItemSc sc{};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int lw = kGU ? (b < 2 ? 0 : 128) + 32 * wave + 16 * (b & 1) + lr : 64 * wave + 16 * b + lr;
+      if constexpr (WF == kMX4) sc.a[b] = asc_lds + lw * kpr + 4 * S + q;
+      if constexpr (WF == kQ4) {
+        const int cpr = p.K / 256, sw = (cpr & (cpr - 1)) == 0 ? cpr - 1 : 0, blk = 4 * S + q;
+        const int i = lw * kpr + (((blk >> 3) ^ (lw & sw)) << 3) + (blk & 7);
+        sc.s[b] = qsc_lds[i];
+        sc.m[b] = qmn_lds[i];
+      }
+    }
+    if constexpr (WF == kMX4) {
       sc.b = bsc_lds + lr * kpr + 4 * S + q;
       sc.bstep = 16 * kpr;
     }
@@ -513,11 +591,15 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * (kAhead - 1)) : "memory");  // super-stage 0 landed
   tie<WF>(at[0]);
   stage_barrier();
+  // item scales: MX pointers into LDS; 4-bit values, read one super-stage ahead
+  ItemSc isc = item_sc(0);
   auto step = [&](int S, auto slot) {
     constexpr int j = decltype(slot)::value;
     const int S2 = min(S + kAhead, nS - 1);
+    const ItemSc cur = isc;
+    isc = item_sc(min(S + 1, nS - 1));
     compute<WF, BM>(at[j], lds + j * kBStage, acc, lr, q, [&](int g) { part(S2, (j + kAhead) % kRing, g); },
-                    mx_sc(S));
+                    cur);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * (kAhead - 1)) : "memory");  // super-stage S + 1 landed
     tie<WF>(at[(j + 1) % kRing]);
     stage_barrier();
@@ -588,7 +670,7 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
 // fp32 accumulators per wave, two register slots of FP4 weights and the FP8
 // token fragments (8 registers each) do not fit in half the register file.
 template <int WF>
-constexpr int big_waves_per_simd() { return WF == kQ4 ? 2 : 1; }
+constexpr int big_waves_per_simd() { return 1; }
 
 // One block per item.  Items of the big-tile list (128-row tiles) and, for
 // 4-bit weights, of the small-tile list (<= 64 rows) share the launch: block b
@@ -600,7 +682,8 @@ template <int WF, bool kGU, bool kSmall>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(big_waves_per_simd<WF>())))
 void big_gemm_kernel(Bp p) {
   __shared__ __attribute__((aligned(1024)))
-  uint8_t lds[ring<WF>() * b_stage_bytes<WF, kBigTileRows>() + (WF == kMX4 ? kMxScaleBytes : 0)];
+  uint8_t lds[ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>() +
+              (WF == kMX4 ? kMxScaleBytes : WF == kQ4 ? kQ4ScaleBytes : 0)];
   const int cols = kGU ? kBN / 2 : kBN;  // output columns per item
   const int per_tile = p.N / cols;
   const int big_items = p.sched[kSchedBig] * per_tile;
@@ -616,7 +699,14 @@ void big_gemm_kernel(Bp p) {
     const int item = xcd * small_px + (slot - big_px);
     if (item >= small_items) return;
     const int32_t* tile = p.sched + kSchedHeader + (size_t)(item / per_tile) * kTileInts;
-    gemm_item<WF, kGU, kTileRows>(p, lds, tile[0], tile[1], tile[2], (item % per_tile) * cols);
+    const int rows = tile[2], n0 = (item % per_tile) * cols;
+    // item height by the tile's rows (uniform over the block)
+    if (WF != kMX4 && rows <= 16)
+      gemm_item<WF, kGU, WF == kMX4 ? 32 : 16>(p, lds, tile[0], tile[1], rows, n0);
+    else if (rows <= 32)
+      gemm_item<WF, kGU, 32>(p, lds, tile[0], tile[1], rows, n0);
+    else
+      gemm_item<WF, kGU, kTileRows>(p, lds, tile[0], tile[1], rows, n0);
   }
 }
 
@@ -632,6 +722,7 @@ hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
   const bool mx = a.wfmt == kMX4;
   if (mx && (a.K % 512 != 0 || a.K > kMxMaxK)) return hipErrorInvalidValue;
+  if (a.wfmt == kQ4 && (a.K % 256 != 0 || a.K > kQ4MaxK)) return hipErrorInvalidValue;
   Bp p{mx ? (const void*)a.act_q : a.act, mx ? (const uint8_t*)a.act_scale : nullptr, a.row_token, a.sched, a.w,
        a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
   // grid: per XCD, slots for an upper bound of each list's items (big tiles

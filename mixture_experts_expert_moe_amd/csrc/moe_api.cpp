@@ -66,8 +66,10 @@ moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // Big tiles (128 rows, register-A / LDS-B kernel) for long prefill
 // chunks with bf16 or 4-bit weights; a host-side rule on T alone.
 // The 4-bit big-tile kernel addresses weights and activations with 32-bit
-// byte offsets; layers too large for that keep the small-tile kernel.
+// byte offsets and keeps an item's scales and mins in LDS (hidden and inter
+// multiples of 256 up to 2048); other layers keep the small-tile kernel.
 bool q4_offsets_fit(const moe_desc* d) {
+  if (d->hidden % 256 || d->inter % 256 || d->hidden > 2048 || d->inter > 2048) return false;
   const int64_t H = d->hidden, I = d->inter, G = d->n_routed + d->n_shared;
   const int64_t r_max = (int64_t)d->max_tokens * (d->top_k + d->n_shared);
   const int64_t lim = (int64_t)1 << 32;
@@ -85,8 +87,11 @@ bool mx_offsets_fit(const moe_desc* d) {
   return G * 2 * I * (H / 2) < lim && (int64_t)d->max_tokens * H < lim && r_max * I < lim;
 }
 
+#ifndef MOE_BIG_MIN_T_Q4
+#define MOE_BIG_MIN_T_Q4 64
+#endif
 bool big_tiles(const moe_desc* d, int32_t T) {
-  if (T < moe::kBigTileMinTokens) return false;
+  if (T < (d->w_dtype == MOE_Q4B32 ? MOE_BIG_MIN_T_Q4 : moe::kBigTileMinTokens)) return false;
   return d->w_dtype == MOE_BF16 || (d->w_dtype == MOE_Q4B32 && q4_offsets_fit(d)) ||
          (d->w_dtype == MOE_MXFP4 && mx_offsets_fit(d));
 }
