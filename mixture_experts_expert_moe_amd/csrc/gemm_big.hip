@@ -76,7 +76,13 @@ constexpr int ring() {
 static_assert(MOE_BIG_RING_Q4 == 3, "ring depth: three 32 KB token stages and the item's scales fill the LDS");
 static_assert(MOE_BIG_RING_MX >= 3 && MOE_BIG_RING_MX <= 4, "ring depth");
 static_assert(MOE_BIG_RING_SHORT >= 2 && MOE_BIG_RING_SHORT <= 4, "ring depth");
-constexpr int kThreads = 256;
+// Waves per block: 4-bit eight (two per SIMD; the 4-bit decode is VALU-bound,
+// and one wave per SIMD issues VALU instructions at well under the SIMD's
+// rate), the other formats four.  Each wave owns 256 / (16 waves) weight
+// fragments of 16 rows.
+template <int WF> constexpr int big_waves() { return WF == kQ4 ? 8 : 4; }
+template <int WF> constexpr int big_threads() { return kWave * big_waves<WF>(); }
+template <int WF> constexpr int frags() { return kBN / 16 / big_waves<WF>(); }
 // Token rows per block: kBigTileRows for the big-tile list, kTileRows for the
 // small-tile list.  Bytes of one token row per super-stage (bf16: 256, E4M3:
 // 128), 16-byte chunks per row, rows per 1 KB DMA instruction; B stage bytes
@@ -105,7 +111,13 @@ constexpr int kQ4ArrayBytes = kBN * (kQ4MaxK / 32) * 2;
 constexpr int kQ4ScaleBytes = 2 * kQ4ArrayBytes;
 __device__ __forceinline__ int mx_a_dma(int K) { return K / 512; }
 template <int BM> __device__ __forceinline__ int mx_b_dma(int K) { return max(1, BM * (K / 512) / 256); }
-template <int WF, int BM> constexpr int b_dma_per_wave() { return b_data_bytes<WF, BM>() / 1024 / 4; }
+// 1 KB DMA instructions per stage (all waves), per wave (at least one: with
+// fewer instructions than waves, wave w repeats instruction w % total, the
+// same bytes to the same place).
+template <int WF, int BM> constexpr int b_dma_total() { return b_data_bytes<WF, BM>() / 1024; }
+template <int WF, int BM> constexpr int b_dma_per_wave() {
+  return b_dma_total<WF, BM>() >= big_waves<WF>() ? b_dma_total<WF, BM>() / big_waves<WF>() : 1;
+}
 // Chunk slot of a row's 16-byte chunk c in LDS: XOR-swizzled by row so that
 // the 16 rows of a fragment read spread over the banks (256-byte rows: all
 // 16 slots; 128-byte rows: two rows per 256 bytes, 8 slots each).
@@ -153,7 +165,7 @@ __device__ __forceinline__ u32x4 gload16(const void* base, uint32_t off) {
 // Vector-memory loads each thread issues per super-stage (LDS DMA + A).
 template <int WF, int BM>
 constexpr int loads_per_stage() {
-  return b_dma_per_wave<WF, BM>() + (WF == kQ4 || WF == kMX4 ? 4 : 16);
+  return b_dma_per_wave<WF, BM>() + (WF == kQ4 || WF == kMX4 ? frags<WF>() : 16);
 }
 
 // One wave's A operand for one super-stage: 4 fragments of 16 weight rows.
@@ -164,21 +176,24 @@ constexpr int loads_per_stage() {
 //          the scale bytes are in LDS.
 template <int WF>
 struct ATile {
-  u32x4 v[4][WF == kQ4 || WF == kMX4 ? 1 : 4];
+  u32x4 v[frags<WF>()][WF == kQ4 || WF == kMX4 ? 1 : 4];
 };
 
 // Part g (0..7) of one super-stage's A loads (the loads are spread over the
-// eight MFMA groups of the previous super-stage).  4-bit and MX: the codes of
-// fragment g / 2 on even g; bf16: fragment g / 2, steps 2 (g % 2) and
-// 2 (g % 2) + 1.
+// eight parts the compute loop issues).  4-bit and MX: the codes of fragment
+// g / (8 / F) when g is a multiple of 8 / F (F fragments per wave); bf16:
+// fragment g / 2, steps 2 (g % 2) and 2 (g % 2) + 1.
 template <int WF, class Row>
-__device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row (&arow)[4], int S, int q, int g) {
-  const int b = g / 2;
+__device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row (&arow)[frags<WF>()], int S, int q,
+                                            int g) {
   if constexpr (WF == kMX4 || WF == kQ4) {
     // 32-bit offsets (the launcher checks that the weights fit)
     static_assert(sizeof(Row) == 4, "4-bit and MX weights use 32-bit offsets");
-    if (g % 2 == 0) a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
+    constexpr int PPF = 8 / frags<WF>();  // parts per fragment
+    const int b = g / PPF;
+    if (g % PPF == 0) a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
   } else {
+    const int b = g / 2;
 #pragma unroll
     for (int kk = 2 * (g % 2); kk < 2 * (g % 2) + 2; ++kk)
       a.v[b][kk] = gload16((const uint16_t*)p.w + arow[b] * p.K + S * kSK + 32 * kk + 8 * q);
@@ -189,26 +204,32 @@ __device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row
 template <int WF>
 __device__ __forceinline__ void tie(ATile<WF>& a) {
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
+  for (int b = 0; b < frags<WF>(); ++b) {
 #pragma unroll
     for (int i = 0; i < (WF == kQ4 || WF == kMX4 ? 1 : 4); ++i) asm volatile("" : "+v"(a.v[b][i]));
   }
 }
 
-// B operand of one super-stage -> LDS, DMA instruction i of the wave (n per
-// wave): it writes the 1 KB at (n wave + i) KB of the stage: rows
-// RPD (n wave + i) + lane / (64 / RPD), chunk slot lane % (64 / RPD), which
-// holds the row's chunk slot ^ b_swz(row).
+// DMA instruction i of wave `wave` for the token rows of one stage: which
+// 1 KB of the stage it writes.
+template <int WF, int BM>
+__device__ __forceinline__ int b_dma_index(int wave, int i) {
+  return (b_dma_per_wave<WF, BM>() * wave + i) % b_dma_total<WF, BM>();
+}
+
+// B operand of one super-stage -> LDS, DMA instruction i of the wave: it
+// writes the 1 KB at d = b_dma_index KB of the stage: rows
+// RPD d + lane / (64 / RPD), chunk slot lane % (64 / RPD), which holds the
+// row's chunk slot ^ b_swz(row).
 template <int WF, int BM, class Src>
 __device__ __forceinline__ void load_b_part(uint8_t* stage, const void* act,
                                             const Src (&src)[b_dma_per_wave<WF, BM>()], int S, int wave, int i) {
-  constexpr int n = b_dma_per_wave<WF, BM>();
   const uint8_t* g;
   if constexpr (sizeof(Src) == 4)
     g = (const uint8_t*)act + (src[i] + (uint32_t)S * b_row_bytes<WF>());  // 32-bit byte offset
   else
     g = (const uint8_t*)src[i] + (size_t)S * b_row_bytes<WF>();
-  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(stage + (n * wave + i) * 1024), 16, 0, 0);
+  __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(stage + b_dma_index<WF, BM>(wave, i) * 1024), 16, 0, 0);
 }
 
 // MX: one 16-byte chunk of item scales -> LDS (lane-consecutive destinations).
@@ -239,7 +260,7 @@ __device__ __forceinline__ int b_chunk(int q, int kk) {
 // A fragment of step kk for weight block b.  4-bit: the dword holds codes
 // 8kk .. 8kk+7 of the lane's block, two per byte (even code in the low nibble).
 template <int WF>
-__device__ __forceinline__ u32x4 a_frag(const ATile<WF>& a, const Q4Block (&qs)[4], int b, int kk) {
+__device__ __forceinline__ u32x4 a_frag(const ATile<WF>& a, const Q4Block (&qs)[frags<WF>()], int b, int kk) {
   if constexpr (WF == kQ4) {
     return q4_decode8(a.v[b][0][kk], qs[b]);  // codes 8kk .. 8kk+7 of the lane's block
   } else {
@@ -268,7 +289,7 @@ struct ItemSc {
 };
 
 template <int WF, int BM, class IssuePart>
-__device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[4][BM / 16], int lr,
+__device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[frags<WF>()][BM / 16], int lr,
                                         int q, IssuePart&& issue_part, const ItemSc& sc = ItemSc{}) {
   constexpr int NG = BM / 64, G = 4 * NG, PPG = G > 0 ? 8 / G : 0;  // groups per step, groups, load parts per group
   if constexpr (WF == kMX4) {
@@ -316,43 +337,43 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
     }
     return;
   }
-  Q4Block qs[4];
+  constexpr int F = frags<WF>();
+  Q4Block qs[F];
   if constexpr (WF == kQ4) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) qs[b] = q4_block(sc.s[b], sc.m[b]);
-    // 4-bit, every item height, one wave per SIMD: while the 4 NC MFMAs of
-    // step kk run, the same wave decodes the weight fragments of step kk + 1
-    // and reads its token fragments from LDS, so the decode (about two VALU
-    // instructions per weight) and the LDS latency hide under the matrix pipe
-    // (or, for short items, the MFMAs under the decode).  sched_group_barrier
-    // pins the interleave: the LDS reads, then one MFMA and a share of the
-    // decode at a time.
-    constexpr int NC = BM / 16, NM = 4 * NC, VPM = (96 + NM - 1) / NM;
+    for (int b = 0; b < F; ++b) qs[b] = q4_block(sc.s[b], sc.m[b]);
+    // 4-bit, every item height: while the F NC MFMAs of step kk run, the
+    // wave decodes its weight fragments of step kk + 1 and reads its token
+    // fragments from LDS, so the decode (about two VALU instructions per
+    // weight) and the LDS latency overlap the matrix pipe; the other wave on
+    // the SIMD fills the gaps.  sched_group_barrier pins the interleave: the
+    // LDS reads, then one MFMA and a share of the decode at a time.
+    constexpr int NC = BM / 16, NM = F * NC, VPM = (24 * F + NM - 1) / NM;
     auto bfr = [&](int kk, int c) {
       return *reinterpret_cast<const u32x4*>(st + (16 * c + lr) * (kSK * 2) + 16 * (b_chunk<WF>(q, kk) ^ lr));
     };
-    u32x4 af[4], bf[NC];
+    u32x4 af[F], bf[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) bf[c] = bfr(0, c);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) af[b] = a_frag<WF>(a, qs, b, 0);
+    for (int b = 0; b < F; ++b) af[b] = a_frag<WF>(a, qs, b, 0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       __builtin_amdgcn_sched_barrier(0);
       issue_part(2 * kk);
       issue_part(2 * kk + 1);
       __builtin_amdgcn_sched_barrier(0);
-      u32x4 an[4], bn[NC];
+      u32x4 an[F], bn[NC];
       if (kk < 3) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) bn[c] = bfr(kk + 1, c);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) an[b] = a_frag<WF>(a, qs, b, kk + 1);
+        for (int b = 0; b < F; ++b) an[b] = a_frag<WF>(a, qs, b, kk + 1);
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[b][c] = mfma_bf16_16x16x32(af[b], bf[c], acc[b][c]);
+        for (int b = 0; b < F; ++b) acc[b][c] = mfma_bf16_16x16x32(af[b], bf[c], acc[b][c]);
       if (kk < 3) {
         __builtin_amdgcn_sched_group_barrier(0x100, NC, 0);  // LDS reads
 #pragma unroll
@@ -366,11 +387,11 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
 #pragma unroll
         for (int c = 0; c < NC; ++c) bf[c] = bn[c];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) af[b] = an[b];
+        for (int b = 0; b < F; ++b) af[b] = an[b];
       }
     }
     return;
-  }
+  } else {
   if constexpr (BM < 64) {
     // Short bf16 items (one or two token blocks): per step kk, two parts of
     // the later loads, the NC token fragments, the four weight fragments and
@@ -435,6 +456,7 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
       for (int b = 0; b < 4; ++b) af[b] = na[b];
     }
   }
+  }  // bf16
 }
 
 __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
@@ -456,22 +478,27 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   constexpr bool k32 = WF == kQ4 || WF == kMX4;  // 32-bit offsets
   using Row = typename std::conditional<k32, uint32_t, size_t>::type;
   using Src = typename std::conditional<k32, uint32_t, const uint8_t*>::type;
-  // A rows of this wave's 4 fragments (GU: gate cols i0.., i0+16.., then the up rows).
-  Row arow[4];
+  // This wave's F weight fragments, as rows of the item's 256 (lw): gate/up:
+  // the first F / 2 are gate rows (item rows < 128: gate columns n0 + lw),
+  // the rest the up rows of the same columns (lw - 128); down: columns n0 + lw.
+  constexpr int F = frags<WF>();
+  auto local_row = [&](int b) {
+    return kGU ? (b < F / 2 ? 0 : 128) + 8 * F * wave + 16 * (b % (F / 2)) + lr : 16 * F * wave + 16 * b + lr;
+  };
+  Row arow[F];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    if constexpr (kGU) {
-      const int i = n0 + 32 * wave + 16 * (b & 1) + lr;
-      arow[b] = (Row)group * 2 * p.N + (b < 2 ? i : p.N + i);
-    } else {
-      arow[b] = (Row)group * p.N + n0 + 64 * wave + 16 * b + lr;
-    }
+  for (int b = 0; b < F; ++b) {
+    const int lw = local_row(b);
+    if constexpr (kGU)
+      arow[b] = (Row)group * 2 * p.N + (lw < 128 ? n0 + lw : p.N + n0 + lw - 128);
+    else
+      arow[b] = (Row)group * p.N + n0 + lw;
   }
   // B sources of this lane's DMA chunks (rows past the tile repeat row 0).
   Src bsrc[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int rr = kRPD * (NB * wave + i) + lane / kLPR;
+    const int rr = kRPD * b_dma_index<WF, BM>(wave, i) + lane / kLPR;
     const int r = rr < rows ? row0 + rr : row0;
     const int chunk = (lane % kLPR) ^ b_swz<WF>(rr);
     if constexpr (k32) {
@@ -524,18 +551,22 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   uint16_t* const qsc_lds = reinterpret_cast<uint16_t*>(lds + ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>());
   uint16_t* const qmn_lds = qsc_lds + kQ4ArrayBytes / 2;
   if constexpr (WF == kQ4) {
-    const int cpr = p.K / 256, n = p.K / 256;  // chunks per row; instructions per wave and array
+    // K chunks per array; instruction i of wave w copies chunks c0 .. c0 + 63,
+    // c0 = 64 (n w + i) mod K (with fewer chunks than lanes in the block, the
+    // later waves repeat the first ones: the same bytes to the same place)
+    constexpr int NW = big_waves<WF>();
+    const int cpr = p.K / 256, n = (p.K + kWave * NW - 1) / (kWave * NW);
     const int sw = (cpr & (cpr - 1)) == 0 ? cpr - 1 : 0;
 #pragma unroll
-    for (int i = 0; i < kQ4MaxK / 256; ++i) {
+    for (int i = 0; i < (kQ4MaxK + kWave * NW - 1) / (kWave * NW); ++i) {
       if (i < n) {
-        const int ci = (wave * n + i) * kWave + lane;  // < 256 cpr
+        const int c0 = ((wave * n + i) * kWave) % p.K, ci = c0 + lane;  // < K = 256 cpr
         const int lw = ci / cpr, part = (ci % cpr) ^ (lw & sw);
         const uint32_t grow = kGU ? (uint32_t)group * 2 * p.N + (lw < 128 ? n0 + lw : p.N + n0 + lw - 128)
                                   : (uint32_t)group * p.N + n0 + lw;
         const uint32_t off = grow * (uint32_t)(kpr * 2) + 16 * part;
-        load_scale_chunk((uint8_t*)qsc_lds + (wave * n + i) * 1024, (const uint8_t*)p.w_scale + off);
-        load_scale_chunk((uint8_t*)qmn_lds + (wave * n + i) * 1024, (const uint8_t*)p.w_min + off);
+        load_scale_chunk((uint8_t*)qsc_lds + c0 * 16, (const uint8_t*)p.w_scale + off);
+        load_scale_chunk((uint8_t*)qmn_lds + c0 * 16, (const uint8_t*)p.w_min + off);
       }
     }
   }
@@ -544,8 +575,8 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   auto item_sc = [&](int S) {
     ItemSc sc{};
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int lw = kGU ? (b < 2 ? 0 : 128) + 32 * wave + 16 * (b & 1) + lr : 64 * wave + 16 * b + lr;
+    for (int b = 0; b < F; ++b) {
+      const int lw = local_row(b);
       if constexpr (WF == kMX4) sc.a[b] = asc_lds + lw * kpr + 4 * S + q;
       if constexpr (WF == kQ4) {
         const int cpr = p.K / 256, sw = (cpr & (cpr - 1)) == 0 ? cpr - 1 : 0, blk = 4 * S + q;
@@ -561,9 +592,9 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
     return sc;
   };
 
-  f32x4 acc[4][NC];
+  f32x4 acc[F][NC];
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < F; ++b)
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -636,11 +667,11 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
     const int r = row0 + tr;
     if constexpr (kGU) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int col = n0 + 32 * wave + 16 * b + 4 * q;
+      for (int b = 0; b < F / 2; ++b) {
+        const int col = n0 + local_row(b) - lr + 4 * q;  // gate fragment b, up fragment b + F / 2
         float v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = silu_fast(acc[b][c][i]) * acc[b + 2][c][i];
+        for (int i = 0; i < 4; ++i) v[i] = silu_fast(acc[b][c][i]) * acc[b + F / 2][c][i];
         if constexpr (WF == kMX4) {
           *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = f32x4{v[0], v[1], v[2], v[3]};
         } else {
@@ -650,14 +681,14 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
       }
     } else if constexpr (WF == kMX4) {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int col = n0 + 64 * wave + 16 * b + 4 * q;
+      for (int b = 0; b < F; ++b) {
+        const int col = n0 + local_row(b) - lr + 4 * q;
         *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = acc[b][c];
       }
     } else {
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int col = n0 + 64 * wave + 16 * b + 4 * q;
+      for (int b = 0; b < F; ++b) {
+        const int col = n0 + local_row(b) - lr + 4 * q;
         u32x2 o = {pack_bf16x2(acc[b][c][0], acc[b][c][1]), pack_bf16x2(acc[b][c][2], acc[b][c][3])};
         *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
       }
@@ -670,7 +701,7 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
 // fp32 accumulators per wave, two register slots of FP4 weights and the FP8
 // token fragments (8 registers each) do not fit in half the register file.
 template <int WF>
-constexpr int big_waves_per_simd() { return 1; }
+constexpr int big_waves_per_simd() { return big_waves<WF>() / 4; }
 
 // One block per item.  Items of the big-tile list (128-row tiles) and, for
 // 4-bit weights, of the small-tile list (<= 64 rows) share the launch: block b
@@ -679,7 +710,7 @@ constexpr int big_waves_per_simd() { return 1; }
 // the CUs that the last big items leave idle, and the column blocks of one
 // row tile (which read the same token rows) share an L2.
 template <int WF, bool kGU, bool kSmall>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(big_waves_per_simd<WF>())))
+__global__ __launch_bounds__(big_threads<WF>()) __attribute__((amdgpu_waves_per_eu(big_waves_per_simd<WF>())))
 void big_gemm_kernel(Bp p) {
   __shared__ __attribute__((aligned(1024)))
   uint8_t lds[ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>() +
@@ -733,11 +764,11 @@ hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   const int64_t blocks = (big_px + small_px) * kXcds;
   if (blocks > (int64_t)INT32_MAX) return hipErrorInvalidValue;
   if (mx)
-    hipLaunchKernelGGL((big_gemm_kernel<kMX4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((big_gemm_kernel<kMX4, kGU, true>), dim3(blocks), dim3(big_threads<kMX4>()), 0, stream, p);
   else if (a.wfmt == kQ4)
-    hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((big_gemm_kernel<kQ4, kGU, true>), dim3(blocks), dim3(big_threads<kQ4>()), 0, stream, p);
   else
-    hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU, true>), dim3(blocks), dim3(kThreads), 0, stream, p);
+    hipLaunchKernelGGL((big_gemm_kernel<kBF16, kGU, true>), dim3(blocks), dim3(big_threads<kBF16>()), 0, stream, p);
   return hipGetLastError();
 }
 
