@@ -131,13 +131,9 @@ hipError_t launch(const GemmArgs& a, hipStream_t stream) {
     case kBF16: return launch_fmt<kBF16, kGU, 4>(a, stream);
     case kI8: return launch_fmt<kI8, kGU, 4>(a, stream);
     case kQ4:
-#ifdef MOE_Q4_GU_SUB2
-      if (a.T >= kQ4DownChunkMinT) return launch_fmt<kQ4, kGU, 2>(a, stream);
-#else
       if constexpr (!kGU) {
         if (a.T >= kQ4DownChunkMinT) return launch_fmt<kQ4, kGU, 2>(a, stream);
       }
-#endif
       return launch_fmt<kQ4, kGU, 4>(a, stream);
     case kMX4: return launch_fmt<kMX4, kGU, 2>(a, stream);  // 32-row items: no spills at two waves per SIMD
     default: return hipErrorInvalidValue;
