@@ -276,7 +276,9 @@ moe_status moe_decode_layer(const moe_desc* desc, int32_t T, const void* x, cons
  * buffers for 16 tokens exceed 8 MiB returns MOE_ERR_UNSUPPORTED (the layer
  * shapes of the pages' model, hidden 2048, 128 experts, take about 1.8 MiB).
  * Every call on one GPU shares that GPU's array and leaves its contents there:
- * calls that overlap on one GPU (other streams, other threads) race. */
+ * calls that overlap on one GPU (other streams, other threads) race.  The
+ * grid-barrier words sit at the start of the array for every desc (zero at
+ * load, valid after each completed call), the other buffers after them. */
 moe_status moe_decode_layer_static(const moe_desc* desc, int32_t T, const void* x, const void* w_router,
                                    const float* bias, const moe_weights* w_gu, const moe_weights* w_down,
                                    const float* residual, int32_t flags, float eps, void* out,

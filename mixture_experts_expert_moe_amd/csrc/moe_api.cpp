@@ -87,11 +87,8 @@ bool mx_offsets_fit(const moe_desc* d) {
   return G * 2 * I * (H / 2) < lim && (int64_t)d->max_tokens * H < lim && r_max * I < lim;
 }
 
-#ifndef MOE_BIG_MIN_T_Q4
-#define MOE_BIG_MIN_T_Q4 64
-#endif
 bool big_tiles(const moe_desc* d, int32_t T) {
-  if (T < (d->w_dtype == MOE_Q4B32 ? MOE_BIG_MIN_T_Q4 : moe::kBigTileMinTokens)) return false;
+  if (T < (d->w_dtype == MOE_Q4B32 ? moe::kBigTileMinTokensQ4 : moe::kBigTileMinTokens)) return false;
   return d->w_dtype == MOE_BF16 || (d->w_dtype == MOE_Q4B32 && q4_offsets_fit(d)) ||
          (d->w_dtype == MOE_MXFP4 && mx_offsets_fit(d));
 }
@@ -417,9 +414,14 @@ moe_status moe_decode_layer_static(const moe_desc* d, int32_t T, const void* x, 
   size_t cap = 0;
   if (moe::decode_static_scratch(&base, &cap) != hipSuccess) return MOE_ERR_HIP;
   if (total > cap) return MOE_ERR_UNSUPPORTED;
+  // The grid-barrier words first, at the same place for every desc: they
+  // stay valid from one call to the next only if no other layout puts its
+  // data there (the rest of the layout depends on the desc's dtypes and sizes).
+  static_assert(MOE_NUM_BUFFERS == 14, "sync is buffer 13");
   void* p[MOE_NUM_BUFFERS];
-  size_t off = 0;
-  for (int i = 0; i < MOE_NUM_BUFFERS; ++i) {
+  size_t off = (sizes[13] + 255) / 256 * 256;
+  p[13] = base;
+  for (int i = 0; i < MOE_NUM_BUFFERS - 1; ++i) {
     p[i] = sizes[i] ? (void*)((char*)base + off) : nullptr;
     off += (sizes[i] + 255) / 256 * 256;
   }
