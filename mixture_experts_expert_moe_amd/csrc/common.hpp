@@ -28,6 +28,7 @@ constexpr int kBigTileRows = 128;   // rows per big tile
 constexpr int kBigTileMin = 128;    // a group needs at least this many rows for big tiles
 constexpr int kBigPartMin = 64;     // a remainder of at least this many rows is one more, partial, big tile
 constexpr int kBigTileMinTokens = 1024;  // big tiles are used for calls with T >= this
+constexpr int kBigTileMinTokensQ4 = 17;  // 4-bit weights: every call past the few-token (decode) sizes
 constexpr int kXcds = 8;          // MI355X: 8 accelerator complex dies, workgroups dealt round-robin
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }

@@ -58,11 +58,13 @@ SMALL = [
     ("q4_e16k4s1_t1024_zipf_big", 256, 512, 16, 4, 1, 1024, "q4", 1.1),
     ("q4_e256k16_t1100_zipf_big", 256, 256, 256, 16, 0, 1100, "q4", 1.1),
     # a prefill chunk of the 4-bit stack (T = 256, the pages' expert shape):
-    # 4-bit calls from 64 tokens on take the big-tile kernel, here mostly with
-    # 16- and 32-row items (the shared expert in two 128-row tiles)
+    # 4-bit calls of more than 16 tokens take the big-tile kernel, here mostly
+    # with 16- and 32-row items (the shared expert in two 128-row tiles); and
+    # both sides of that limit
     ("q4_e128k8s1_t256_h2048_chunk", 2048, 512, 128, 8, 1, 256, "q4", 0.0),
-    ("q4_e32k4s1_t64_h2048", 2048, 512, 32, 4, 1, 64, "q4", 0.0),
-    ("q4_e32k4s1_t63_h2048", 2048, 512, 32, 4, 1, 63, "q4", 0.0),
+    ("q4_e32k4s1_t17_h2048", 2048, 512, 32, 4, 1, 17, "q4", 0.0),
+    ("q4_e32k4s1_t16_h2048", 2048, 512, 32, 4, 1, 16, "q4", 0.0),
+    ("q4_e128k8s1_t40_h2048_last_chunk", 2048, 512, 128, 8, 1, 40, "q4", 0.0),
     # MXFP4 weights x MXFP8 activations (scaled FP4 x FP8 MFMA): 16-pair gate/up
     # items (T <= 16, few-token routing), 32-row items with ragged tails, a
     # Zipf-skewed routing, and T >= 1024 (no big tiles for this format)
@@ -92,7 +94,7 @@ def check_permute(g, ref_perm):
     np.testing.assert_array_equal(g.token_row(), token_row)
     head, small, big = g.sched()
     # The tiles cover every group's rows exactly once: small tiles of <= 64 rows,
-    # big tiles of 64..128 rows (only from T = 1024 on; 4-bit weights: T = 64),
+    # big tiles of 64..128 rows (only from T = 1024 on; 4-bit weights: T = 17),
     # big tiles first within a group.
     covered = np.zeros(offsets[-1], np.int32)
     for tiles, lo, hi in ((small, 1, 64), (big, 64, 128)):
@@ -101,7 +103,7 @@ def check_permute(g, ref_perm):
             covered[r0:r0 + n] += 1
     assert np.all(covered == 1)
     T = g.T
-    if T < (64 if g.spec.wt == "q4" else 1024):
+    if T < (17 if g.spec.wt == "q4" else 1024):
         assert len(big) == 0
 
 
