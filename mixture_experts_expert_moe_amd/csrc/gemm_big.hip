@@ -1,41 +1,40 @@
-// Big-tile grouped GEMMs for groups with many rows (compute-bound prefill):
-// gate/up + SwiGLU and down over the big tiles of the schedule, bf16 or 4-bit
-// block weights.
+// Big-tile grouped GEMMs: gate/up + SwiGLU and down over the big tiles of
+// the schedule (and, in the same launch, its small tiles), for bf16, 4-bit
+// block and MXFP4 weights.
 //
 // Where a group has a hundred rows or more the layer is bound by the matrix
-// cores, not by weight bytes.  A block owns 256 weight rows x 128 token rows
-// and walks K in super-stages of 128:
-//  * the token rows (operand B, shared by all four waves) are copied from
+// cores, not by weight bytes.  A block owns 256 weight rows x up to 128 token
+// rows (items of 128, 64, 32 or 16 token rows, by the tile) and walks K in
+// super-stages of 128:
+//  * the token rows (operand B, shared by the block's waves) are copied from
 //    global memory straight into LDS with global_load_lds_dwordx4, into a ring
 //    of stages, in a row-major layout whose 16-byte chunks are
 //    XOR-swizzled by row so that fragment reads avoid bank conflicts;
-//  * each wave owns 64 weight rows (operand A) and loads them from global
-//    memory directly into registers in the MFMA fragment layout, into a ring
-//    of register tiles; 4-bit codes are dequantised in registers right
-//    before the MFMAs that use them, so every weight byte is read and decoded
-//    once per block and never passes through LDS;
-//  * the loads of super-stage S + 2 are issued while S is computed, so two
-//    super-stages of loads are in flight behind the MFMAs (bf16; see below
-//    for 4-bit);
-//  * v_mfma_f32_16x16x32_bf16 accumulates a 64 x 128 tile per wave.
-// That is the bf16 layout (one block, one wave per SIMD, per CU).  With 4-bit
-// weights the ring holds two super-stages (loads one ahead), operand
-// fragments are not prefetched and addresses are 32-bit offsets, so a wave
-// fits in half the register file and two blocks share each CU: while one
-// wave decodes 4-bit codes on the VALU the other's MFMAs run, and one block's
-// prologue and epilogue overlap the other's main loop.
-// For 4-bit weights the K order inside a super-stage is permuted so that each
-// lane's 16-byte load is one whole 32-code block (one scale, one min); the
-// token fragments are read from LDS in the same order, which leaves the dot
-// products unchanged.
+//  * each wave owns 64 weight rows (bf16, MX: four waves) or 32 (4-bit: eight
+//    waves, two per SIMD) as operand A and loads them from global memory
+//    directly into registers in the MFMA fragment layout, into a ring of
+//    register tiles; 4-bit codes are dequantised in registers right before
+//    the MFMAs that use them, so every weight byte is read and decoded once
+//    per block and never passes through LDS;
+//  * the loads of super-stage S + ring - 1 are issued while S is computed;
+//  * v_mfma_f32_16x16x32_bf16 accumulates (weight rows) x (token rows) per
+//    wave.
+// 4-bit: the decode is about two VALU instructions per weight, and one wave
+// per SIMD issues VALU instructions well below the SIMD's rate, hence two
+// waves per SIMD; while the MFMAs of step k run, the wave decodes the weight
+// fragments of step k + 1.  The K order inside a super-stage is permuted so
+// that each lane's 16-byte load is one whole 32-code block (one scale, one
+// min); the token fragments are read from LDS in the same order, which
+// leaves the dot products unchanged.
 // MXFP4 weights (E2M1, one E8M0 scale per 32) against MXFP8 token rows take
 // the same loop with one scaled FP4 x FP8 MFMA (16x16x128) per fragment pair
 // and super-stage: a lane's 16-byte weight load is its whole 32-element block,
 // nothing is decoded, and the token rows are 128 bytes per super-stage in LDS.
-// The scale bytes of the item's 256 weight rows and of its token rows (K / 32
-// per row) are copied into LDS once, in 16-byte chunks, before the loop: read
-// per super-stage from global memory, one byte per lane, they were half of the
-// cache lines the loop touched and held its load issue back.
+// The item's scales (MX: E8M0 bytes of its weight and token rows; 4-bit: the
+// fp16 scales and mins of its weight rows) are copied into LDS once, in
+// 16-byte chunks, before the loop: read per super-stage from global memory,
+// each row's scale lines were touched over the whole item, fell out of L2 and
+// held the load issue back.
 //
 // The shared expert and every routed expert go through the same launch; the
 // grouping itself is the point of the pages' "concatenated-expert" fix
@@ -92,25 +91,18 @@ template <int WF> constexpr int b_row_bytes() { return WF == kMX4 ? kSK : kSK * 
 template <int WF> constexpr int b_row_chunks() { return b_row_bytes<WF>() / 16; }
 template <int WF> constexpr int b_rows_per_dma() { return 1024 / b_row_bytes<WF>(); }
 template <int WF, int BM> constexpr int b_data_bytes() { return BM * b_row_bytes<WF>(); }
-// MX scale area: each wave's DMA writes 64 dwords (256 bytes); lane l of wave
-// w holds the 4 scale bytes of token row BM / 4 * w + l % (BM / 4) (lanes
-// past BM / 4 repeat rows, so that every lane of the DMA is active).
 template <int WF, int BM> constexpr int b_stage_bytes() { return b_data_bytes<WF, BM>(); }
 // MX item scales in LDS (K <= kMxMaxK, K % 512 == 0): the 256 weight rows'
-// bytes, then the token rows', each row K / 32 bytes.  DMA instructions per
-// wave: weight rows 256 K / 512 chunks of 16 bytes over 4 waves x 64 lanes;
-// token rows BM K / 512 chunks (at least one instruction per wave; lanes past
-// the last chunk repeat it into the padding).
+// bytes, then the token rows', each row K / 32 bytes, copied in 16-byte
+// chunks (256 K / 512 and BM K / 512 of them) spread over the block's lanes.
 constexpr int kMxMaxK = 2048;
 constexpr int kMxScaleBytes = kBN * (kMxMaxK / 32) + kBigTileRows * (kMxMaxK / 32);
 // 4-bit item scales and mins in LDS (K <= kQ4MaxK, K % 256 == 0): the 256
-// weight rows' fp16 scales, then their fp16 mins, K / 32 of each per row; the
-// 16-byte DMA chunks of one array are K per item, K / 256 instructions per wave.
+// weight rows' fp16 scales, then their fp16 mins, K / 32 of each per row; K
+// 16-byte DMA chunks per array, spread over the block's lanes.
 constexpr int kQ4MaxK = 2048;
 constexpr int kQ4ArrayBytes = kBN * (kQ4MaxK / 32) * 2;
 constexpr int kQ4ScaleBytes = 2 * kQ4ArrayBytes;
-__device__ __forceinline__ int mx_a_dma(int K) { return K / 512; }
-template <int BM> __device__ __forceinline__ int mx_b_dma(int K) { return max(1, BM * (K / 512) / 256); }
 // 1 KB DMA instructions per stage (all waves), per wave (at least one: with
 // fewer instructions than waves, wave w repeats instruction w % total, the
 // same bytes to the same place).
@@ -292,6 +284,7 @@ template <int WF, int BM, class IssuePart>
 __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f32x4 (&acc)[frags<WF>()][BM / 16], int lr,
                                         int q, IssuePart&& issue_part, const ItemSc& sc = ItemSc{}) {
   constexpr int NG = BM / 64, G = 4 * NG, PPG = G > 0 ? 8 / G : 0;  // groups per step, groups, load parts per group
+  constexpr int F = frags<WF>();
   if constexpr (WF == kMX4) {
     // One scaled MFMA per (weight block, token block), in groups of GW token
     // blocks; the next group's two FP8 halves and scale bytes are read from
@@ -302,9 +295,9 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
     // addresses of a token block differ from block 0's by a constant.
     const uint8_t* h0 = st + lr * b_row_bytes<WF>() + 16 * (b_chunk<WF>(q, 0) ^ b_swz<WF>(lr));
     const uint8_t* h1 = st + lr * b_row_bytes<WF>() + 16 * (b_chunk<WF>(q, 1) ^ b_swz<WF>(lr));
-    uint32_t as[4];
+    uint32_t as[F];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) as[b] = *sc.a[b];
+    for (int b = 0; b < F; ++b) as[b] = *sc.a[b];
     struct BG {
       u32x4 b0[GW], b1[GW];
       uint32_t bs[GW];
@@ -329,7 +322,7 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
 #pragma unroll
       for (int i = 0; i < GW; ++i)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < F; ++b)
           acc[b][GW * g + i] =
               mfma_mx4_mx8_16x16x128(a.v[b][0], as[b], cur.b0[i], cur.b1[i], cur.bs[i], acc[b][GW * g + i]);
       __builtin_amdgcn_sched_barrier(0);
@@ -337,7 +330,6 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
     }
     return;
   }
-  constexpr int F = frags<WF>();
   Q4Block qs[F];
   if constexpr (WF == kQ4) {
 #pragma unroll
@@ -516,22 +508,27 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   uint8_t* const bsc_lds = asc_lds + kBN * (kMxMaxK / 32);
   const int kpr = p.K / 32;
   if constexpr (WF == kMX4) {
-    const int cpr = p.K / 512, na = mx_a_dma(p.K), nb = mx_b_dma<BM>(p.K);
+    // weight rows: 256 cpr chunks (a multiple of 64), instruction i of wave w
+    // copies chunks c0 .. c0 + 63, c0 = 64 (na w + i) mod 256 cpr (later waves
+    // repeat the first ones when there are fewer chunks than lanes); token
+    // rows: BM cpr chunks, lanes past the last one repeat it into the padding
+    constexpr int NW = big_waves<WF>();
+    const int cpr = p.K / 512, ca = 256 * cpr, cb = BM * cpr;
+    const int na = (ca + kWave * NW - 1) / (kWave * NW), nb = max(1, cb / (kWave * NW));
 #pragma unroll
-    for (int i = 0; i < kMxMaxK / 512; ++i) {
+    for (int i = 0; i < (kBN * (kMxMaxK / 512) + kWave * NW - 1) / (kWave * NW); ++i) {
       if (i < na) {
-        const int ci = (wave * na + i) * kWave + lane;  // < 256 cpr
+        const int c0 = ((wave * na + i) * kWave) % ca, ci = c0 + lane;
         const int lw = ci / cpr, part = ci % cpr;
         const uint32_t grow = kGU ? (uint32_t)group * 2 * p.N + (lw < 128 ? n0 + lw : p.N + n0 + lw - 128)
                                   : (uint32_t)group * p.N + n0 + lw;
-        load_scale_chunk(asc_lds + (wave * na + i) * 1024,
-                         (const uint8_t*)p.w_scale + grow * (uint32_t)kpr + 16 * part);
+        load_scale_chunk(asc_lds + c0 * 16, (const uint8_t*)p.w_scale + grow * (uint32_t)kpr + 16 * part);
       }
     }
 #pragma unroll
-    for (int i = 0; i < kBigTileRows * (kMxMaxK / 512) / 256; ++i) {
+    for (int i = 0; i < (kBigTileRows * (kMxMaxK / 512) + kWave * NW - 1) / (kWave * NW); ++i) {
       if (i < nb) {
-        const int ci = min((wave * nb + i) * kWave + lane, BM * cpr - 1);
+        const int ci = min((wave * nb + i) * kWave + lane, cb - 1);
         const int rr = ci / cpr, part = ci % cpr;
         const int r = rr < rows ? row0 + rr : row0;
         const uint32_t src_row = kGU ? (uint32_t)min(max(p.row_token[r], 0), p.T - 1) : (uint32_t)r;
