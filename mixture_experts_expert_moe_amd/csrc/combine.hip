@@ -68,18 +68,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   __shared__ float s_part[4];
   const int t = blockIdx.x;
   const int kS = k + S;
-  // out[t][c0 .. c0+8) into acc
+  // out[t][c0 .. c0+8) into acc.  The rows' loads go out kBatch at a time,
+  // unconditionally (a missing row, r < 0, reads row 0 and is not added), so
+  // that they are in flight together; the sum keeps the slot order.
+  constexpr int kBatch = 9;
   auto chunk = [&](int c0, float (&acc)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < kS; ++j) {
-      const int r = token_row[(size_t)t * kS + j];
-      if (r < 0) continue;
-      const float g = (j < k) ? topk_w[(size_t)t * k + j] : 1.0f;
-      float v[8];
-      load8<kYF32>(y, (size_t)r * H + c0, v);
+    for (int j0 = 0; j0 < kS; j0 += kBatch) {
+      int r[kBatch];
+      float g[kBatch], v[kBatch][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+      for (int u = 0; u < kBatch; ++u) {
+        const int j = j0 + u;
+        r[u] = j < kS ? token_row[(size_t)t * kS + j] : -1;
+        g[u] = j < k ? topk_w[(size_t)t * k + j] : 1.0f;
+        load8<kYF32>(y, (size_t)max(r[u], 0) * H + c0, v[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (r[u] < 0) continue;  // uniform over the block
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(g[u], v[u][i], acc[i]);
+      }
     }
     if (residual) {
       float v[8];
