@@ -21,8 +21,8 @@
 //    wave.
 // 4-bit: the decode is about two VALU instructions per weight, and one wave
 // per SIMD issues VALU instructions well below the SIMD's rate, hence two
-// waves per SIMD; while the MFMAs of step k run, the wave decodes the weight
-// fragments of step k + 1.  The K order inside a super-stage is permuted so
+// waves per SIMD; the weight fragments of step k + 1 are decoded alongside
+// the MFMAs of step k.  The K order inside a super-stage is permuted so
 // that each lane's 16-byte load is one whole 32-code block (one scale, one
 // min); the token fragments are read from LDS in the same order, which
 // leaves the dot products unchanged.
@@ -334,13 +334,13 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
   if constexpr (WF == kQ4) {
 #pragma unroll
     for (int b = 0; b < F; ++b) qs[b] = q4_block(sc.s[b], sc.m[b]);
-    // 4-bit, every item height: while the F NC MFMAs of step kk run, the
-    // wave decodes its weight fragments of step kk + 1 and reads its token
-    // fragments from LDS, so the decode (about two VALU instructions per
-    // weight) and the LDS latency overlap the matrix pipe; the other wave on
-    // the SIMD fills the gaps.  sched_group_barrier pins the interleave: the
-    // LDS reads, then one MFMA and a share of the decode at a time.
-    constexpr int NC = BM / 16, NM = F * NC, VPM = (24 * F + NM - 1) / NM;
+    // 4-bit, every item height: the F NC MFMAs of step kk go out together
+    // with the decode of the wave's weight fragments of step kk + 1 and the
+    // LDS reads of its token fragments, so the decode (about two VALU
+    // instructions per weight) and the LDS latency overlap the matrix pipe;
+    // the other wave on the SIMD fills the gaps (the compiler's order within
+    // a step measured as good as one pinned with sched_group_barrier).
+    constexpr int NC = BM / 16;
     auto bfr = [&](int kk, int c) {
       return *reinterpret_cast<const u32x4*>(st + (16 * c + lr) * (kSK * 2) + 16 * (b_chunk<WF>(q, kk) ^ lr));
     };
@@ -366,14 +366,6 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
       for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int b = 0; b < F; ++b) acc[b][c] = mfma_bf16_16x16x32(af[b], bf[c], acc[b][c]);
-      if (kk < 3) {
-        __builtin_amdgcn_sched_group_barrier(0x100, NC, 0);  // LDS reads
-#pragma unroll
-        for (int i = 0; i < NM; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);  // a share of the decode
-        }
-      }
       __builtin_amdgcn_sched_barrier(0);
       if (kk < 3) {
 #pragma unroll
