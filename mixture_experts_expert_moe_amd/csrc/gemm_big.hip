@@ -124,6 +124,11 @@ constexpr bool item_height_ok() {
   return (BM == 128 || BM == 64 || BM == 32 || (BM == 16 && WF != kMX4)) && b_dma_per_wave<WF, BM>() >= 1;
 }
 
+// Down items of two 256-column blocks (4-bit and MX; the bf16 kernel has no
+// registers to spare for a store inside its loop).
+template <int WF, bool kGU>
+constexpr bool kTwoBlocks() { return !kGU && WF != kBF16; }
+
 struct Bp {
   const void* act;          // x [T][K] (gate/up, gathered by row_token) or h [R][K] (down), bf16 (MX: E4M3)
   const uint8_t* act_scale; // MX: E8M0 bytes [rows][K / 32] of act
@@ -134,6 +139,7 @@ struct Bp {
   const void* w_min;
   void* out;                // h [R][N] or y [R][N], bf16 (MX: fp32)
   int K, N, T, R;
+  int ncb;                  // 256-column weight blocks per item (down: 2 when they fit, else 1)
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -176,19 +182,19 @@ struct ATile {
 // g / (8 / F) when g is a multiple of 8 / F (F fragments per wave); bf16:
 // fragment g / 2, steps 2 (g % 2) and 2 (g % 2) + 1.
 template <int WF, class Row>
-__device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row (&arow)[frags<WF>()], int S, int q,
-                                            int g) {
+__device__ __forceinline__ void load_a_part(const Bp& p, ATile<WF>& a, const Row (&arow)[frags<WF>()], Row roff,
+                                            int S, int q, int g) {
   if constexpr (WF == kMX4 || WF == kQ4) {
     // 32-bit offsets (the launcher checks that the weights fit)
     static_assert(sizeof(Row) == 4, "4-bit and MX weights use 32-bit offsets");
     constexpr int PPF = 8 / frags<WF>();  // parts per fragment
     const int b = g / PPF;
-    if (g % PPF == 0) a.v[b][0] = gload16(p.w, arow[b] * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
+    if (g % PPF == 0) a.v[b][0] = gload16(p.w, (arow[b] + roff) * (uint32_t)(p.K / 2) + S * (kSK / 2) + 16 * q);
   } else {
     const int b = g / 2;
 #pragma unroll
     for (int kk = 2 * (g % 2); kk < 2 * (g % 2) + 2; ++kk)
-      a.v[b][kk] = gload16((const uint16_t*)p.w + arow[b] * p.K + S * kSK + 32 * kk + 8 * q);
+      a.v[b][kk] = gload16((const uint16_t*)p.w + (arow[b] + roff) * p.K + S * kSK + 32 * kk + 8 * q);
   }
 }
 
@@ -445,8 +451,12 @@ __device__ __forceinline__ void compute(const ATile<WF>& a, const uint8_t* st, f
 
 __device__ __forceinline__ float silu_fast(float g) { return g / (1.0f + __expf(-g)); }
 
-// One item: weight columns [n0, n0 + 256) (gate/up: 128 gate/up pairs) of
-// group `group` against token rows [row0, row0 + rows) (rows <= BM).
+// One item: weight columns [n0, n0 + 256 ncb) (gate/up: 128 gate/up pairs,
+// ncb = 1) of group `group` against token rows [row0, row0 + rows)
+// (rows <= BM).  With ncb = 2 (down) the item walks K once per 256-column
+// block, the ring running on from the first block into the second, so the
+// second block's first loads are in flight while the first block's results
+// are stored.
 template <int WF, bool kGU, int BM>
 __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, int row0, int rows, int n0) {
   constexpr int kBStage = b_stage_bytes<WF, BM>(), NC = BM / 16, NB = b_dma_per_wave<WF, BM>();
@@ -466,6 +476,7 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   // the first F / 2 are gate rows (item rows < 128: gate columns n0 + lw),
   // the rest the up rows of the same columns (lw - 128); down: columns n0 + lw.
   constexpr int F = frags<WF>();
+  const int ncb = kTwoBlocks<WF, kGU>() ? p.ncb : 1;
   auto local_row = [&](int b) {
     return kGU ? (b < F / 2 ? 0 : 128) + 8 * F * wave + 16 * (b % (F / 2)) + lr : 16 * F * wave + 16 * b + lr;
   };
@@ -500,12 +511,12 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   uint8_t* const bsc_lds = asc_lds + kBN * (kMxMaxK / 32);
   const int kpr = p.K / 32;
   if constexpr (WF == kMX4) {
-    // weight rows: 256 cpr chunks (a multiple of 64), instruction i of wave w
-    // copies chunks c0 .. c0 + 63, c0 = 64 (na w + i) mod 256 cpr (later waves
+    // weight rows: 256 ncb cpr chunks (a multiple of 64), instruction i of
+    // wave w copies chunks c0 .. c0 + 63, c0 = 64 (na w + i) mod ca (later waves
     // repeat the first ones when there are fewer chunks than lanes); token
     // rows: BM cpr chunks, lanes past the last one repeat it into the padding
     constexpr int NW = big_waves<WF>();
-    const int cpr = p.K / 512, ca = 256 * cpr, cb = BM * cpr;
+    const int cpr = p.K / 512, ca = 256 * ncb * cpr, cb = BM * cpr;
     const int na = (ca + kWave * NW - 1) / (kWave * NW), nb = max(1, cb / (kWave * NW));
 #pragma unroll
     for (int i = 0; i < (kBN * (kMxMaxK / 512) + kWave * NW - 1) / (kWave * NW); ++i) {
@@ -540,16 +551,17 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   uint16_t* const qsc_lds = reinterpret_cast<uint16_t*>(lds + ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>());
   uint16_t* const qmn_lds = qsc_lds + kQ4ArrayBytes / 2;
   if constexpr (WF == kQ4) {
-    // K chunks per array; instruction i of wave w copies chunks c0 .. c0 + 63,
-    // c0 = 64 (n w + i) mod K (with fewer chunks than lanes in the block, the
-    // later waves repeat the first ones: the same bytes to the same place)
+    // ncb K chunks per array (256 ncb rows); instruction i of wave w copies
+    // chunks c0 .. c0 + 63, c0 = 64 (n w + i) mod (ncb K) (with fewer chunks
+    // than lanes in the block, the later waves repeat the first ones: the
+    // same bytes to the same place)
     constexpr int NW = big_waves<WF>();
-    const int cpr = p.K / 256, n = (p.K + kWave * NW - 1) / (kWave * NW);
+    const int cpr = p.K / 256, chunks = ncb * p.K, n = (chunks + kWave * NW - 1) / (kWave * NW);
     const int sw = (cpr & (cpr - 1)) == 0 ? cpr - 1 : 0;
 #pragma unroll
     for (int i = 0; i < (kQ4MaxK + kWave * NW - 1) / (kWave * NW); ++i) {
       if (i < n) {
-        const int c0 = ((wave * n + i) * kWave) % p.K, ci = c0 + lane;  // < K = 256 cpr
+        const int c0 = ((wave * n + i) * kWave) % chunks, ci = c0 + lane;  // < 256 ncb cpr
         const int lw = ci / cpr, part = (ci % cpr) ^ (lw & sw);
         const uint32_t grow = kGU ? (uint32_t)group * 2 * p.N + (lw < 128 ? n0 + lw : p.N + n0 + lw - 128)
                                   : (uint32_t)group * p.N + n0 + lw;
@@ -559,13 +571,16 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
       }
     }
   }
-  // This lane's item scales of super-stage S (block 4 S + q): weight fragment
-  // b's row; MX also token block 0's row (lr), token block c at + 16 c kpr.
-  auto item_sc = [&](int S) {
+  // This lane's item scales of super-stage S (column block S / nSK, K block
+  // 4 (S % nSK) + q): weight fragment b's row; MX also token block 0's row
+  // (lr), token block c at + 16 c kpr.
+  const int nSK = p.K / kSK;
+  auto item_sc = [&](int S0) {
     ItemSc sc{};
+    const int cbk = S0 / nSK, S = S0 - cbk * nSK;
 #pragma unroll
     for (int b = 0; b < F; ++b) {
-      const int lw = local_row(b);
+      const int lw = local_row(b) + 256 * cbk;
       if constexpr (WF == kMX4) sc.a[b] = asc_lds + lw * kpr + 4 * S + q;
       if constexpr (WF == kQ4) {
         const int cpr = p.K / 256, sw = (cpr & (cpr - 1)) == 0 ? cpr - 1 : 0, blk = 4 * S + q;
@@ -587,6 +602,45 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
 #pragma unroll
     for (int c = 0; c < NC; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Results of column block cbk: fragment b's D[i][j] (i: weight row, j:
+  // token) is in lane j + 16 * (i / 4), register i % 4.
+  auto store = [&](int cbk) {
+  #pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int tr = 16 * c + lr;
+      if (tr >= rows) continue;
+      const int r = row0 + tr;
+      if constexpr (kGU) {
+  #pragma unroll
+        for (int b = 0; b < F / 2; ++b) {
+          const int col = n0 + 256 * cbk + local_row(b) - lr + 4 * q;  // gate fragment b, up fragment b + F / 2
+          float v[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = silu_fast(acc[b][c][i]) * acc[b + F / 2][c][i];
+          if constexpr (WF == kMX4) {
+            *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = f32x4{v[0], v[1], v[2], v[3]};
+          } else {
+            u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
+          }
+        }
+      } else if constexpr (WF == kMX4) {
+  #pragma unroll
+        for (int b = 0; b < F; ++b) {
+          const int col = n0 + 256 * cbk + local_row(b) - lr + 4 * q;
+          *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = acc[b][c];
+        }
+      } else {
+  #pragma unroll
+        for (int b = 0; b < F; ++b) {
+          const int col = n0 + 256 * cbk + local_row(b) - lr + 4 * q;
+          u32x2 o = {pack_bf16x2(acc[b][c][0], acc[b][c][1]), pack_bf16x2(acc[b][c][2], acc[b][c][3])};
+          *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
+        }
+      }
+    }
+  };
+
   // Ring of kRing super-stages.  step(S, j) computes S from slot j while
   // issuing the loads of S + kAhead (clamped to the last super-stage, so that
   // every step issues the same number of loads and the wait below is a
@@ -594,12 +648,13 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   // closing S - 1 freed; it then waits until only the loads issued after
   // those of S + 1 are outstanding (none with a ring of two).
   ATile<WF> at[kRing];
-  const int nS = p.K / kSK;
+  const int nS = ncb * nSK;
   constexpr int L = loads_per_stage<WF, BM>();
-  // Part g (0..7) of the loads of super-stage S into slot j.
+  // Part g (0..7) of the loads of super-stage S (column block S / nSK) into slot j.
   auto part = [&](int S, int j, int g) {
-    if (g < NB) load_b_part<WF, BM>(lds + j * kBStage, p.act, bsrc, S, wave, g);
-    load_a_part<WF>(p, at[j], arow, S, q, g);
+    const int cbk = S / nSK, sk = S - cbk * nSK;
+    if (g < NB) load_b_part<WF, BM>(lds + j * kBStage, p.act, bsrc, sk, wave, g);
+    load_a_part<WF>(p, at[j], arow, (Row)(256 * cbk), sk, q, g);
   };
   auto issue = [&](int S, int j) {
 #pragma unroll
@@ -623,6 +678,15 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L * (kAhead - 1)) : "memory");  // super-stage S + 1 landed
     tie<WF>(at[(j + 1) % kRing]);
     stage_barrier();
+    if constexpr (kTwoBlocks<WF, kGU>()) {
+      if (S + 1 < nS && S + 1 == nSK) {  // the first of two column blocks is done
+        store(0);
+#pragma unroll
+        for (int b = 0; b < F; ++b)
+#pragma unroll
+          for (int c = 0; c < NC; ++c) acc[b][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
   };
   // Whole rounds of the ring, then the remaining super-stages (fewer than
   // kRing; nested, so that every path through the waits is one the ring takes).
@@ -647,42 +711,7 @@ __device__ __forceinline__ void gemm_item(const Bp& p, uint8_t* lds, int group, 
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int j = 0; j < kRing; ++j) tie<WF>(at[j]);
-  // Epilogue: fragment b's D[i][j] (i: weight row, j: token) is in lane
-  // j + 16 * (i / 4), register i % 4.
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int tr = 16 * c + lr;
-    if (tr >= rows) continue;
-    const int r = row0 + tr;
-    if constexpr (kGU) {
-#pragma unroll
-      for (int b = 0; b < F / 2; ++b) {
-        const int col = n0 + local_row(b) - lr + 4 * q;  // gate fragment b, up fragment b + F / 2
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = silu_fast(acc[b][c][i]) * acc[b + F / 2][c][i];
-        if constexpr (WF == kMX4) {
-          *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = f32x4{v[0], v[1], v[2], v[3]};
-        } else {
-          u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
-        }
-      }
-    } else if constexpr (WF == kMX4) {
-#pragma unroll
-      for (int b = 0; b < F; ++b) {
-        const int col = n0 + local_row(b) - lr + 4 * q;
-        *reinterpret_cast<f32x4*>((float*)p.out + (size_t)r * p.N + col) = acc[b][c];
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < F; ++b) {
-        const int col = n0 + local_row(b) - lr + 4 * q;
-        u32x2 o = {pack_bf16x2(acc[b][c][0], acc[b][c][1]), pack_bf16x2(acc[b][c][2], acc[b][c][3])};
-        *reinterpret_cast<u32x2*>((uint16_t*)p.out + (size_t)r * p.N + col) = o;
-      }
-    }
-  }
+  store(ncb - 1);
 }
 
 // Waves per SIMD (blocks per CU): bf16 one (three-deep ring, operand
@@ -704,7 +733,7 @@ void big_gemm_kernel(Bp p) {
   __shared__ __attribute__((aligned(1024)))
   uint8_t lds[ring<WF, kBigTileRows>() * b_stage_bytes<WF, kBigTileRows>() +
               (WF == kMX4 ? kMxScaleBytes : WF == kQ4 ? kQ4ScaleBytes : 0)];
-  const int cols = kGU ? kBN / 2 : kBN;  // output columns per item
+  const int cols = kGU ? kBN / 2 : kBN * p.ncb;  // output columns per item
   const int per_tile = p.N / cols;
   const int big_items = p.sched[kSchedBig] * per_tile;
   const int small_items = kSmall ? p.sched[kSchedSmall] * per_tile : 0;
@@ -738,13 +767,20 @@ template <bool kGU>
 hipError_t launch(const GemmArgs& a, bool with_small, hipStream_t stream) {
   if (a.wfmt != kBF16 && a.wfmt != kQ4 && a.wfmt != kMX4) return hipErrorInvalidValue;
   if (!with_small) return hipErrorInvalidValue;  // the small tiles always run in the same launch
-  const int cols = kGU ? kBN / 2 : kBN;
-  if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
   const bool mx = a.wfmt == kMX4;
   if (mx && (a.K % 512 != 0 || a.K > kMxMaxK)) return hipErrorInvalidValue;
   if (a.wfmt == kQ4 && (a.K % 256 != 0 || a.K > kQ4MaxK)) return hipErrorInvalidValue;
+  // down items of long calls take two 256-column blocks where N allows and
+  // their scales fit the item's LDS copy (short K: the per-item prologue and
+  // epilogue weigh most there); shorter calls keep one, for enough items to
+  // spread evenly over the CUs
+  const int max_k = mx ? kMxMaxK : kQ4MaxK;
+  const int ncb = !kGU && a.wfmt != kBF16 && a.T >= kBigTileMinTokens && a.N % (2 * kBN) == 0 && 2 * a.K <= max_k
+                      ? 2 : 1;
+  const int cols = kGU ? kBN / 2 : kBN * ncb;
+  if (a.N % cols != 0 || a.K % kSK != 0) return hipErrorInvalidValue;
   Bp p{mx ? (const void*)a.act_q : a.act, mx ? (const uint8_t*)a.act_scale : nullptr, a.row_token, a.sched, a.w,
-       a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R};
+       a.w_scale, a.w_min, a.out, a.K, a.N, a.T, a.R, ncb};
   // grid: per XCD, slots for an upper bound of each list's items (big tiles
   // hold >= kBigPartMin rows)
   const int64_t per_tile = a.N / cols;

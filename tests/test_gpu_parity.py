@@ -57,6 +57,8 @@ SMALL = [
     ("q4_e8k2s1_t1100_big", 256, 256, 8, 2, 1, 1100, "q4", 0.0),
     ("q4_e16k4s1_t1024_zipf_big", 256, 512, 16, 4, 1, 1024, "q4", 1.1),
     ("q4_e256k16_t1100_zipf_big", 256, 256, 256, 16, 0, 1100, "q4", 1.1),
+    # hidden 512: down items of two 256-column blocks (calls of >= 1024 tokens)
+    ("q4_e8k2s1_t1100_h512_big", 512, 256, 8, 2, 1, 1100, "q4", 0.0),
     # a prefill chunk of the 4-bit stack (T = 256, the pages' expert shape):
     # 4-bit calls of more than 16 tokens take the big-tile kernel, here mostly
     # with 16- and 32-row items (the shared expert in two 128-row tiles); and
