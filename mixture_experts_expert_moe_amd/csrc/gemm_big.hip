@@ -49,13 +49,11 @@
 namespace moe {
 namespace {
 
-constexpr int kBN = 256;                 // weight rows per block (4 waves x 64)
+constexpr int kBN = 256;                 // weight rows per block (4 waves x 64; 4-bit: 8 x 32)
 constexpr int kSK = 128;                 // K per super-stage
-// Super-stages resident (LDS stages and A register tiles).  bf16: a ring of
-// three, one block (one wave per SIMD) per CU.  4-bit: a ring of two with
-// 32-bit offsets and no operand prefetch, so that a wave fits in half the
-// register file and two blocks share a CU, each covering the other's load
-// latency, prologue and epilogue.
+// Super-stages resident (LDS stages and A register tiles), one block per CU:
+// bf16 and 4-bit a ring of three (4-bit: with the item's scales, the three
+// 32 KB token stages of a 128-row item fill the LDS), MX four.
 #ifndef MOE_BIG_RING_Q4
 #define MOE_BIG_RING_Q4 3
 #endif
