@@ -19,7 +19,10 @@
 namespace moe {
 namespace {
 
-constexpr int kRouteWaves = 8;  // waves per block; each takes an eighth of H
+// Waves per block, each taking an equal share of H: eight for partial sums
+// over a slice of H (few blocks), four for whole logits (many blocks: T = 2048
+// logits 36 -> 30 us with four waves, two batches of four steps each).
+template <bool kPartial> constexpr int route_waves() { return kPartial ? 8 : 4; }
 
 // One block computes logits for 16 tokens x 16 experts.  Lane l of a wave
 // holds token/expert (l % 16) and loads 8 consecutive h (one 16-byte load for
@@ -29,12 +32,13 @@ constexpr int kRouteWaves = 8;  // waves per block; each takes an eighth of H
 // 16 z .. 16 z + 15 and writes its fp64 partial sums, partials[slice][t][e],
 // instead of logits.
 template <bool kF32, bool kPartial>
-__global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const void* __restrict__ x,
+__global__ __launch_bounds__(kWave* route_waves<kPartial>()) void route_logits_kernel(const void* __restrict__ x,
                                                                         const void* __restrict__ wr,
                                                                         const float* __restrict__ bias,
                                                                         float* __restrict__ logits,
                                                                         double* __restrict__ partials, int T, int H,
                                                                         int E) {
+  constexpr int kRouteWaves = route_waves<kPartial>();
   __shared__ double part[kRouteWaves][16][17];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int t0 = (kPartial ? blockIdx.z : blockIdx.x) * 16, e0 = blockIdx.y * 16;
@@ -44,8 +48,8 @@ __global__ __launch_bounds__(kWave* kRouteWaves) void route_logits_kernel(const 
   const int hq = hs / kRouteWaves;
   const int hbeg = (kPartial ? blockIdx.x * hs : 0) + wave * hq;
   f64x4 acc = {0.0, 0.0, 0.0, 0.0}, acc2 = {0.0, 0.0, 0.0, 0.0};  // two independent MFMA chains
-  // Batches of 8 steps of 32 h: all loads of a batch are issued before its MFMAs.
-  constexpr int kNb = 8;
+  // Batches of kNb steps of 32 h: all loads of a batch are issued before its MFMAs.
+  constexpr int kNb = kPartial ? 8 : 4;
   for (int h0 = hbeg; h0 < hbeg + hq; h0 += 32 * kNb) {
     u32x4 xv[kNb][kF32 ? 2 : 1], wv[kNb][kF32 ? 2 : 1];
 #pragma unroll
@@ -158,10 +162,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   if (split) {
     dim3 grid(kRouteSplit, eb, tb);
     if (a.act_f32)
-      hipLaunchKernelGGL((route_logits_kernel<true, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+      hipLaunchKernelGGL((route_logits_kernel<true, true>), grid, dim3(kWave * route_waves<true>()), 0, stream, a.x,
                          a.w_router, nullptr, nullptr, a.partials, a.T, a.H, a.E);
     else
-      hipLaunchKernelGGL((route_logits_kernel<false, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+      hipLaunchKernelGGL((route_logits_kernel<false, true>), grid, dim3(kWave * route_waves<true>()), 0, stream, a.x,
                          a.w_router, nullptr, nullptr, a.partials, a.T, a.H, a.E);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
@@ -171,10 +175,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   }
   dim3 grid(tb, eb);
   if (a.act_f32)
-    hipLaunchKernelGGL((route_logits_kernel<true, false>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+    hipLaunchKernelGGL((route_logits_kernel<true, false>), grid, dim3(kWave * route_waves<false>()), 0, stream, a.x,
                        a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
   else
-    hipLaunchKernelGGL((route_logits_kernel<false, false>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+    hipLaunchKernelGGL((route_logits_kernel<false, false>), grid, dim3(kWave * route_waves<false>()), 0, stream, a.x,
                        a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -186,10 +190,10 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
 hipError_t launch_route_partials(const RouteArgs& a, double* partials, int slices, hipStream_t stream) {
   dim3 grid(slices, (a.E + 15) / 16);
   if (a.act_f32)
-    hipLaunchKernelGGL((route_logits_kernel<true, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+    hipLaunchKernelGGL((route_logits_kernel<true, true>), grid, dim3(kWave * route_waves<true>()), 0, stream, a.x,
                        a.w_router, nullptr, nullptr, partials, a.T, a.H, a.E);
   else
-    hipLaunchKernelGGL((route_logits_kernel<false, true>), grid, dim3(kWave * kRouteWaves), 0, stream, a.x,
+    hipLaunchKernelGGL((route_logits_kernel<false, true>), grid, dim3(kWave * route_waves<true>()), 0, stream, a.x,
                        a.w_router, nullptr, nullptr, partials, a.T, a.H, a.E);
   return hipGetLastError();
 }
