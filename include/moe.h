@@ -204,9 +204,11 @@ moe_status moe_route_permute(const moe_desc* desc, int32_t T, const void* x, con
                              const float* bias, const moe_buffers* bufs, hipStream_t stream);
 
 /* Gate/up projection of every permuted row plus SwiGLU, all groups in one
- * launch over the tile schedule (for T >= 1024 with bf16, 4-bit or MXFP4
- * weights, a launch of the big-tile kernel that takes the 128-row tiles and
- * the shorter ones):
+ * launch over the tile schedule (for T >= 1024 with bf16 or MXFP4 weights
+ * and T > 16 with Q4B32 weights, a launch of the big-tile kernel that takes
+ * the 128-row tiles and the shorter ones; for those calls a token's rounding
+ * may depend on the sizes of the groups it shares the call with, results
+ * staying deterministic):
  *   h[r][i] = silu(x_t . Wg[g][i]) * (x_t . Wu[g][i]),  t = row_token[r], g = group of r.
  * Float weights: MFMA with fp32 accumulation, h stored in the h dtype.
  * I8 weights: exact int32 accumulation of x_q . w, then a = (fp32(acc) * x_scale[t]) * scale[g][n]
