@@ -150,10 +150,18 @@ hipError_t decode_static_scratch(void** ptr, size_t* bytes);
 // Word of the sync buffer that a timed-out barrier wait sets to nonzero.
 constexpr int kDecodeStatusWord = 64 * 10;
 
-// Dynamic LDS bytes the permutation kernel needs for T tokens and E experts:
-// a 32-bit word of token bits plus a 16-bit prefix per (expert, 32 tokens).
-inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)((T + 31) / 32) * (size_t)E * 6; }
+// The permutation kernel keeps, per expert, a row of ceil(T / 32) 32-bit
+// words of token bits plus a 16-bit prefix per word in LDS.  The row stride is
+// made odd where that still fits, so the rows of 64 consecutive experts start
+// in 64 different LDS banks (with 64 words per row, T = 2048, every row would
+// start in the same bank and a wave's 64 lanes would collide on it).
 constexpr size_t kPermuteMaxLds = 60 * 1024;
+inline int permute_word_stride(int64_t T, int64_t E) {
+  const int64_t W = (T + 31) / 32;
+  return (int)((W | 1) * E * 6 <= (int64_t)kPermuteMaxLds ? (W | 1) : W);
+}
+// Dynamic LDS bytes the permutation kernel needs for T tokens and E experts.
+inline size_t permute_lds_bytes(int64_t T, int64_t E) { return (size_t)permute_word_stride(T, E) * (size_t)E * 6; }
 
 // Tile schedule capacity for R_max rows over G groups: small tiles first,
 // then the big-tile list (every big tile holds at least 64 rows).

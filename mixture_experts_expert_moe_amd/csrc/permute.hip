@@ -9,7 +9,9 @@
 //
 // One workgroup of 16 waves, all in LDS:
 //  1. per-expert token bitmap: bit t of bits[e] is set when token t chose e
-//     (each (token, slot) pair ORs one bit, so the bitmap is order-independent);
+//     (each (token, slot) pair ORs one bit, so the bitmap is order-independent;
+//     rows at an odd stride where it fits, so that lanes with different
+//     experts hit different banks);
 //  2. per expert, an exclusive prefix of the popcounts of its 32-token words
 //     (one wave per expert, a wave-wide scan over the words);
 //  3. group offsets by a wave-wide scan over the groups, and the tile list:
@@ -30,9 +32,9 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t* __
                                                                int32_t* __restrict__ row_token,
                                                                int32_t* __restrict__ token_row,
                                                                int32_t* __restrict__ sched, int T, int E, int k,
-                                                               int S, int big_on, int big_start) {
+                                                               int S, int big_on, int big_start, int Ws) {
   extern __shared__ uint32_t lds[];
-  permute_block(topk_ids, offsets, row_token, token_row, sched, T, E, k, S, big_on, big_start, lds);
+  permute_block(topk_ids, offsets, row_token, token_row, sched, T, E, k, S, big_on, big_start, Ws, lds);
 }
 
 // One block per row.
@@ -88,7 +90,8 @@ __global__ __launch_bounds__(256) void quant_mx8_kernel(const void* __restrict__
 hipError_t launch_permute(const PermuteArgs& a, hipStream_t stream) {
   const size_t lds = permute_lds_bytes(a.T, a.E);
   hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, stream, a.topk_ids, a.offsets, a.row_token,
-                     a.token_row, a.sched, a.T, a.E, a.k, a.S, a.big_on ? 1 : 0, a.big_start);
+                     a.token_row, a.sched, a.T, a.E, a.k, a.S, a.big_on ? 1 : 0, a.big_start,
+                     permute_word_stride(a.T, a.E));
   return hipGetLastError();
 }
 

@@ -304,29 +304,33 @@ __device__ __forceinline__ int seg_incl_scan(int v) {
 // Per-expert exclusive prefix of the popcounts of its W <= kSeg words, and
 // its total: each wave pass takes 64 / kSeg experts, one lane per word.
 template <int kSeg>
-__device__ __forceinline__ void prefix_words(const uint32_t* bits, uint16_t* pre, int32_t* s_cnt, int E, int W) {
+__device__ __forceinline__ void prefix_words(const uint32_t* bits, uint16_t* pre, int32_t* s_cnt, int E, int W,
+                                             int Ws) {
   constexpr int kPer = kWave / kSeg;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   for (int e0 = wave * kPer; e0 < E; e0 += kPermWaves * kPer) {
     const int e = e0 + lane / kSeg, w = lane % kSeg;
     const bool in = e < E && w < W;
-    const int c = in ? __popc(bits[e * W + w]) : 0;
+    const int c = in ? __popc(bits[e * Ws + w]) : 0;
     const int inc = seg_incl_scan<kSeg>(c);
-    if (in) pre[e * W + w] = (uint16_t)(inc - c);
+    if (in) pre[e * Ws + w] = (uint16_t)(inc - c);
     if (e < E && w == kSeg - 1) s_cnt[e] = inc;
   }
 }
 
 // The permutation by one block of kPermThreads threads (all in LDS; `lds` is
-// permute_lds_bytes(T, E) bytes of shared memory).  topk_ids may point to
-// global or shared memory.
+// permute_lds_bytes(T, E) bytes of shared memory, Ws = permute_word_stride(T,
+// E) the row stride of the bitmap).  topk_ids may point to global or shared
+// memory.
+constexpr int kIdBatch = 16;  // ids per thread in flight at once (T * k <= 16384 in one batch)
+
 __device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* __restrict__ offsets,
                                               int32_t* __restrict__ row_token, int32_t* __restrict__ token_row,
                                               int32_t* __restrict__ sched, int T, int E, int k, int S, int big_on,
-                                              int big_start, uint32_t* lds) {
-  const int W = (T + 31) / 32;                       // 32-token words per expert
-  uint32_t* bits = lds;                              // [E][W]
-  uint16_t* pre = (uint16_t*)(lds + (size_t)E * W);  // [E][W] exclusive popcount prefix
+                                              int big_start, int Ws, uint32_t* lds) {
+  const int W = (T + 31) / 32;                        // 32-token words per expert
+  uint32_t* bits = lds;                               // [E][Ws]
+  uint16_t* pre = (uint16_t*)(lds + (size_t)E * Ws);  // [E][Ws] exclusive popcount prefix
   __shared__ int32_t s_off[kMaxGroups + 1];
   __shared__ int32_t s_tile[kMaxGroups + 1];
   __shared__ int32_t s_cnt[kMaxGroups];
@@ -335,12 +339,22 @@ __device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int pairs = T * k;
 
-  for (int i = threadIdx.x; i < E * W; i += kPermThreads) bits[i] = 0u;
+  for (int i = threadIdx.x; i < E * Ws; i += kPermThreads) bits[i] = 0u;
   __syncthreads();
-  // 1. bitmap
-  for (int i = threadIdx.x; i < pairs; i += kPermThreads) {
-    const int e = topk_ids[i], t = i / k;
-    if ((unsigned)e < (unsigned)E) atomicOr(&bits[e * W + t / 32], 1u << (t % 32));
+  // 1. bitmap.  Each thread issues kIdBatch loads of ids before the first
+  //    atomic that needs one, so their latencies overlap.
+  for (int i0 = threadIdx.x; i0 < pairs; i0 += kPermThreads * kIdBatch) {
+    int ids[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int i = i0 + u * kPermThreads;
+      ids[u] = i < pairs ? topk_ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int e = ids[u], t = (i0 + u * kPermThreads) / k;
+      if ((unsigned)e < (unsigned)E) atomicOr(&bits[e * Ws + t / 32], 1u << (t % 32));
+    }
   }
   __syncthreads();
   // 2. per-expert prefix over words (a single word: prefix 0, count = popcount)
@@ -351,20 +365,20 @@ __device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* 
     }
   } else if (W <= kWave) {
     // 64 / seg experts per wave pass, one lane per word (seg = the power of two >= W)
-    if (W <= 2) prefix_words<2>(bits, pre, s_cnt, E, W);
-    else if (W <= 4) prefix_words<4>(bits, pre, s_cnt, E, W);
-    else if (W <= 8) prefix_words<8>(bits, pre, s_cnt, E, W);
-    else if (W <= 16) prefix_words<16>(bits, pre, s_cnt, E, W);
-    else if (W <= 32) prefix_words<32>(bits, pre, s_cnt, E, W);
-    else prefix_words<64>(bits, pre, s_cnt, E, W);
+    if (W <= 2) prefix_words<2>(bits, pre, s_cnt, E, W, Ws);
+    else if (W <= 4) prefix_words<4>(bits, pre, s_cnt, E, W, Ws);
+    else if (W <= 8) prefix_words<8>(bits, pre, s_cnt, E, W, Ws);
+    else if (W <= 16) prefix_words<16>(bits, pre, s_cnt, E, W, Ws);
+    else if (W <= 32) prefix_words<32>(bits, pre, s_cnt, E, W, Ws);
+    else prefix_words<64>(bits, pre, s_cnt, E, W, Ws);
   } else for (int e = wave; e < E; e += kPermWaves) {
     int base = 0;
     for (int w0 = 0; w0 < W; w0 += kWave) {
       const int w = w0 + lane;
-      const int c = w < W ? __popc(bits[e * W + w]) : 0;
+      const int c = w < W ? __popc(bits[e * Ws + w]) : 0;
       int tot;
       const int ex = wave_excl_scan(c, &tot);
-      if (w < W) pre[e * W + w] = (uint16_t)(base + ex);
+      if (w < W) pre[e * Ws + w] = (uint16_t)(base + ex);
       base += tot;
     }
     if (lane == 0) s_cnt[e] = base;
@@ -499,16 +513,27 @@ __device__ __forceinline__ void permute_block(const int32_t* topk_ids, int32_t* 
       t[3] = 0;
     }
   }
-  // 4. rows
-  for (int i = threadIdx.x; i < pairs; i += kPermThreads) {
-    const int e = topk_ids[i], t = i / k, j = i % k;
-    int row = -1;
-    if ((unsigned)e < (unsigned)E) {
-      const int w = e * W + t / 32;
-      row = s_off[e] + pre[w] + __popc(bits[w] & ((1u << (t % 32)) - 1u));
-      row_token[row] = t;
+  // 4. rows (ids loaded in batches as in 1)
+  for (int i0 = threadIdx.x; i0 < pairs; i0 += kPermThreads * kIdBatch) {
+    int ids[kIdBatch];
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int i = i0 + u * kPermThreads;
+      ids[u] = i < pairs ? topk_ids[i] : -1;
     }
-    token_row[(size_t)t * kS + j] = row;
+#pragma unroll
+    for (int u = 0; u < kIdBatch; ++u) {
+      const int i = i0 + u * kPermThreads;
+      if (i >= pairs) break;
+      const int e = ids[u], t = i / k, j = i % k;
+      int row = -1;
+      if ((unsigned)e < (unsigned)E) {
+        const int w = e * Ws + t / 32;
+        row = s_off[e] + pre[w] + __popc(bits[w] & ((1u << (t % 32)) - 1u));
+        row_token[row] = t;
+      }
+      token_row[(size_t)t * kS + j] = row;
+    }
   }
   if (S) {
     for (int t = threadIdx.x; t < T; t += kPermThreads) {
