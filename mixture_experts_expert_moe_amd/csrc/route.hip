@@ -20,8 +20,8 @@ namespace moe {
 namespace {
 
 // Waves per block, each taking an equal share of H: eight for partial sums
-// over a slice of H (few blocks), four for whole logits (many blocks: T = 2048
-// logits 36 -> 30 us with four waves, two batches of four steps each).
+// over a slice of H (few blocks), four for whole logits (many blocks, but
+// fewer than one 32 x 32 tile per CU, where route_logits32_kernel takes over).
 template <bool kPartial> constexpr int route_waves() { return kPartial ? 8 : 4; }
 
 // One block computes logits for 16 tokens x 16 experts.  Lane l of a wave
@@ -120,6 +120,96 @@ __global__ __launch_bounds__(kWave* route_waves<kPartial>()) void route_logits_k
   }
 }
 
+// Whole logits of 32 tokens x 32 experts per block, for calls with at least
+// one such tile per CU.  Each of the kRoute32Waves waves takes an equal share
+// of H and keeps four 16 x 16 accumulators (token half x expert half), so each
+// x or router element it converts to fp64 feeds two MFMAs instead of one (the
+// 16 x 16 blocks above convert both operands of every MFMA); lanes load and
+// order K as above.  The waves' fp64 sums are added in wave order in LDS and
+// rounded once.  (T = 2048, H = 2048, E = 128: 27.5 -> 21.8 us; below one tile
+// per CU the 16 x 16 blocks are faster, as each block here keeps its CU's
+// matrix cores busy for about 20 us.)
+constexpr int kRoute32Waves = 8;
+constexpr int kRoute32Batch = 2;  // 32-h steps whose loads are issued together
+constexpr int kRoute32HMult = 32 * kRoute32Batch * kRoute32Waves;  // H must be a multiple
+
+template <bool kF32>
+__global__ __launch_bounds__(kWave* kRoute32Waves) void route_logits32_kernel(const void* __restrict__ x,
+                                                                             const void* __restrict__ wr,
+                                                                             const float* __restrict__ bias,
+                                                                             float* __restrict__ logits, int T,
+                                                                             int H, int E) {
+  constexpr int V = kF32 ? 2 : 1;  // 16-byte loads per 8 elements
+  __shared__ double part[kRoute32Waves][32][33];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int r = lane % 16, q = lane / 16;
+  const int row[4] = {min(t0 + r, T - 1), min(t0 + 16 + r, T - 1), min(e0 + r, E - 1), min(e0 + 16 + r, E - 1)};
+  const int hq = H / kRoute32Waves, hbeg = wave * hq;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
+  for (int h0 = hbeg; h0 < hbeg + hq; h0 += 32 * kRoute32Batch) {
+    u32x4 v[kRoute32Batch][4][V];  // [step][x lo, x hi, w lo, w hi][load]
+#pragma unroll
+    for (int u = 0; u < kRoute32Batch; ++u) {
+      const int hh = h0 + 32 * u + 8 * q;
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        const void* base = o < 2 ? x : wr;
+        if constexpr (kF32) {
+          const float* p = (const float*)base + (size_t)row[o] * H + hh;
+          v[u][o][0] = ld16(p);
+          v[u][o][V - 1] = ld16(p + 4);
+        } else {
+          v[u][o][0] = ld16((const uint16_t*)base + (size_t)row[o] * H + hh);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kRoute32Batch; ++u) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        double d[4];
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+          if constexpr (kF32) {
+            d[o] = (double)__uint_as_float(v[u][o][s / 4][s % 4]);
+          } else {
+            const uint32_t w2 = v[u][o][0][s / 2];
+            d[o] = (double)__uint_as_float(s % 2 ? (w2 & 0xffff0000u) : (w2 << 16));
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(d[i], d[2 + j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+  // D layout as above: register k of lane l holds row 4 k + l / 16, column l % 16
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) part[wave][16 * i + 4 * k + q][16 * j + r] = acc[i][j][k];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 32 * 32; idx += kWave * kRoute32Waves) {
+    const int tt = idx / 32, ee = idx % 32;
+    if (t0 + tt < T && e0 + ee < E) {
+      double sum = part[0][tt][ee];
+#pragma unroll
+      for (int w = 1; w < kRoute32Waves; ++w) sum += part[w][tt][ee];
+      float lv = (float)sum;
+      if (bias) lv = __fadd_rn(lv, bias[e0 + ee]);
+      logits[(size_t)(t0 + tt) * E + e0 + ee] = lv;
+    }
+  }
+}
+
 // One wave per token: the rank-count top-k and gates of route_permute.hpp.
 // kSlices > 0: the token's logits are first summed from kSlices fp64
 // partials in slice order, rounded once (+ bias), and written out.
@@ -173,13 +263,24 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
                        a.partials, a.bias, a.logits, a.topk_ids, a.topk_w, a.T, a.E, a.k);
     return hipGetLastError();
   }
-  dim3 grid(tb, eb);
-  if (a.act_f32)
-    hipLaunchKernelGGL((route_logits_kernel<true, false>), grid, dim3(kWave * route_waves<false>()), 0, stream, a.x,
-                       a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
-  else
-    hipLaunchKernelGGL((route_logits_kernel<false, false>), grid, dim3(kWave * route_waves<false>()), 0, stream, a.x,
-                       a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
+  const int tb32 = (a.T + 31) / 32, eb32 = (a.E + 31) / 32;
+  if (tb32 * eb32 >= 256 && a.H % kRoute32HMult == 0) {
+    dim3 grid(tb32, eb32);
+    if (a.act_f32)
+      hipLaunchKernelGGL(route_logits32_kernel<true>, grid, dim3(kWave * kRoute32Waves), 0, stream, a.x, a.w_router,
+                         a.bias, a.logits, a.T, a.H, a.E);
+    else
+      hipLaunchKernelGGL(route_logits32_kernel<false>, grid, dim3(kWave * kRoute32Waves), 0, stream, a.x, a.w_router,
+                         a.bias, a.logits, a.T, a.H, a.E);
+  } else {
+    dim3 grid(tb, eb);
+    if (a.act_f32)
+      hipLaunchKernelGGL((route_logits_kernel<true, false>), grid, dim3(kWave * route_waves<false>()), 0, stream, a.x,
+                         a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
+    else
+      hipLaunchKernelGGL((route_logits_kernel<false, false>), grid, dim3(kWave * route_waves<false>()), 0, stream, a.x,
+                         a.w_router, a.bias, a.logits, nullptr, a.T, a.H, a.E);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(route_topk_kernel<0>, dim3((a.T + 3) / 4), dim3(256), 0, stream, a.logits, nullptr, nullptr,

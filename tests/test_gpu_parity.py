@@ -374,6 +374,19 @@ def test_route_ties_and_zero_token(T, fused):
         assert tied == sorted(tied), (t, ids[t])
 
 
+# Whole logits in 32 x 32 blocks (calls with at least 256 such blocks and H a
+# multiple of 512): fp32 activations (32 experts, T = 8200) and bf16 with a
+# Zipf router bias (128 experts, T = 2047); both T leave a ragged last block.
+@pytest.mark.parametrize("E, k, T, wt, zipf", [(32, 4, 8200, "f32", 0.0), (128, 8, 2047, "bf16", 1.1)],
+                         ids=["f32_e32_t8200", "bf16_e128_t2047_bias"])
+def test_route_whole_logits_32x32(E, k, T, wt, zipf):
+    d = case_inputs(512, 256, E, k, 0, T, wt, zipf, seed=13)
+    say("route 32x32 E", E, "T", T, wt)
+    g = gh.GpuLayer(d)
+    g.route()
+    check_route(g, d, oracle.route(d["x"], d["w_router"], k, d.get("bias")))
+
+
 def test_layer_mx4_zipf_prefill_full():
     """MXFP4 weights x MXFP8 activations at T = 2048 with Zipf-skewed routing,
     every token: the x and h codes bit for bit, every h and y row, then the
