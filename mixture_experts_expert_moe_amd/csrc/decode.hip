@@ -74,29 +74,28 @@ __device__ __forceinline__ void st_rx(uint32_t* p, uint32_t v) {
 // Grid-wide barrier (see the top of the file), in two halves so that a block
 // can send loads that do not depend on the other blocks (the next phase's
 // weights) between its arrival and its wait.  Counters only grow; with
-// per_xcd a power of two their wrap-around keeps every modulus.  The
-// generation read before arriving is returned to thread 0.
-__device__ uint32_t grid_arrive(uint32_t* sync, int per_xcd) {
+// per_xcd a power of two their wrap-around keeps every modulus.  `gen` is
+// the generation word's value before this barrier completes: thread 0 reads
+// it once at the start of the launch (it cannot advance before this block
+// arrives) and counts it up after each wait, so arriving costs only the
+// counter atomics (re-reading it at each arrival put one more memory round
+// trip on the path of the last block to arrive).
+__device__ void grid_arrive(uint32_t* sync, int per_xcd, uint32_t gen) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have completed
   __syncthreads();
-  uint32_t g0 = 0;
   if (threadIdx.x == 0) {
-    uint32_t* gen = sync + kGenWord;
-    g0 = ld_rx(gen);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // g0 read before this block arrives
     const uint32_t old = add_rx(sync + kXcdWord + 64 * (blockIdx.x % kXcds), 1u);
     if (old % (uint32_t)per_xcd == (uint32_t)per_xcd - 1u) {
       const uint32_t o2 = add_rx(sync + kTopWord, 1u);
-      if (o2 % kXcds == kXcds - 1) st_rx(gen, g0 + 1u);
+      if (o2 % kXcds == kXcds - 1) st_rx(sync + kGenWord, gen + 1u);
     }
   }
-  return g0;
 }
-__device__ void grid_wait(uint32_t* sync, uint32_t g0, long long spin_ns) {
+__device__ void grid_wait(uint32_t* sync, uint32_t& gen, long long spin_ns) {
   if (threadIdx.x == 0) {
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();  // 100 MHz
     const uint64_t lim = (uint64_t)spin_ns / 10u;
-    while (ld_rx(sync + kGenWord) == g0) {
+    while (ld_rx(sync + kGenWord) == gen) {
       __builtin_amdgcn_s_sleep(1);
       if (__builtin_amdgcn_s_memrealtime() - t0 > lim) {
         st_rx(sync + kDecodeStatusWord, 1u);
@@ -104,10 +103,12 @@ __device__ void grid_wait(uint32_t* sync, uint32_t g0, long long spin_ns) {
       }
     }
   }
+  ++gen;
   __syncthreads();
 }
-__device__ void grid_barrier(uint32_t* sync, int per_xcd, long long spin_ns) {
-  grid_wait(sync, grid_arrive(sync, per_xcd), spin_ns);
+__device__ void grid_barrier(uint32_t* sync, int per_xcd, uint32_t& gen, long long spin_ns) {
+  grid_arrive(sync, per_xcd, gen);
+  grid_wait(sync, gen, spin_ns);
 }
 
 // Loads of data another block of this launch wrote: buffer loads with the
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
   const int NB = gridDim.x, per_xcd = NB / kXcds;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const bool lead = blockIdx.x == 0;
+  uint32_t gen = tid == 0 ? ld_rx(a.sync + kGenWord) : 0u;  // barrier generation (thread 0)
   uint16_t* xin = L.rows_bf16();  // [T][H] bf16 layer input
 
   // ---- P0: the layer input in LDS; int8 codes; router partial sums ------------
@@ -314,7 +316,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
   {
     // the int8 codes are only needed from P2 on: they are made while this
     // block waits at the barrier
-    const uint32_t g0 = grid_arrive(a.sync, per_xcd);
+    grid_arrive(a.sync, per_xcd, gen);
     if constexpr (WF == kI8) {
       // per-token codes of the int8 path: token t gets P = 8 / (the power of
       // two >= T) waves (one wave per token from 8 tokens on), which split its
@@ -393,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
         }
       }
     }
-    grid_wait(a.sync, g0, a.spin_ns);
+    grid_wait(a.sync, gen, a.spin_ns);
   }
 
   // ---- P1: logits, top-k, permutation (every block, in LDS) ---------------------
@@ -528,9 +530,9 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
         n0 = (it % ipd) * 64;
       }
       if (base == 0) {
-        const uint32_t g0 = grid_arrive(a.sync, per_xcd);
+        grid_arrive(a.sync, per_xcd, gen);
         di.issue(p, g, n0, qw, act);
-        grid_wait(a.sync, g0, a.spin_ns);
+        grid_wait(a.sync, gen, a.spin_ns);
       } else {
         __syncthreads();  // the previous round's rows and reductions have been read
         di.issue(p, g, n0, qw, act);
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
       di.template finish<true>(p, g, row0, rows, n0, red, qw, act);
     }
   }
-  grid_barrier(a.sync, per_xcd, a.spin_ns);
+  grid_barrier(a.sync, per_xcd, gen, a.spin_ns);
 
   // ---- P4: combine (+ residual): unit (token t, 256 columns) on one wave --------
   // out[t][c] = sum_j gate[t][j] * y[row(t, j)][c] (slots in order, the shared

@@ -568,6 +568,56 @@ __device__ __forceinline__ void permute_few_block_t(const int32_t* topk_ids, int
   __shared__ uint32_t s_hmask[kFewTokens + 1][kMaskWords];  // groups of each height
   const int G = E + S, kS = k + S, pairs = T * k;
   const int tid = threadIdx.x;
+  if (T == 1) {
+    // One token: every touched group holds one row, so the counts below
+    // reduce to ranks among the token's experts.  The row of expert e, its
+    // group offset and its tile slot (all heights are 1: slots by group
+    // index) are all the number of chosen experts below e; the shared group
+    // comes last.  Wave 0 ranks the ids (k <= 16 lane reads each); then every
+    // thread takes group offsets.
+    __shared__ int32_t s_one[16];
+    if (tid < kWave) {
+      const int e = tid < k ? topk_ids[tid] : -1;
+      const bool v = (unsigned)e < (unsigned)E;
+      int row = 0;
+      for (int l = 0; l < k; ++l) {
+        const int el = __shfl(e, l);
+        row += ((unsigned)el < (unsigned)E && el < e) ? 1 : 0;
+      }
+      const int nv = (int)__popcll(__ballot(v));
+      if (tid < k) {
+        s_one[tid] = v ? e : -1;
+        token_row[tid] = v ? row : -1;
+        if (v) {
+          row_token[row] = 0;
+          int32_t* t4 = sched + kSchedHeader + (size_t)row * kTileInts;
+          t4[0] = e;
+          t4[1] = row;
+          t4[2] = 1;
+          t4[3] = 0;
+        }
+      }
+      if (tid == 0 && S) {
+        token_row[k] = nv;
+        row_token[nv] = 0;
+        int32_t* t4 = sched + kSchedHeader + (size_t)nv * kTileInts;
+        t4[0] = E;
+        t4[1] = nv;
+        t4[2] = 1;
+        t4[3] = 0;
+      }
+      if (tid < kSchedHeader)
+        sched[tid] = tid == kSchedSmall ? nv + S : tid == kSchedGroups ? G : tid == kSchedRows ? nv + S
+                   : tid == kSchedBigStart ? big_start : 0;
+    }
+    __syncthreads();
+    for (int g = tid; g <= G; g += NT) {
+      int off = 0;
+      for (int l = 0; l < k; ++l) off += (unsigned)s_one[l] < (unsigned)min(g, E) ? 1 : 0;
+      offsets[g] = off + (g > E ? 1 : 0);
+    }
+    return;
+  }
   // 1. keys (padded to a multiple of 4 with keys above every real key); clear the height tables
   const int pairs4 = (pairs + 3) & ~3;
   for (int i = tid; i < pairs4; i += NT) {
