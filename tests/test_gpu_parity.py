@@ -300,6 +300,12 @@ FUSED_ROUTE = [
     ("bf16_e8k8s1_t3_h256", 256, 256, 8, 8, 1, 3, "bf16", 0.0),
     ("bf16_e256k16_t16", 1024, 256, 256, 16, 0, 16, "bf16", 0.0),
     ("mx4_e128k8s1_t5", 2048, 512, 128, 8, 1, 5, "mx4", 0.0),
+    # one token without a shared expert: k = 16 of 256, and k = E
+    ("bf16_e256k16_t1", 1024, 256, 256, 16, 0, 1, "bf16", 0.0),
+    ("bf16_e8k8_t1", 256, 256, 8, 8, 0, 1, "bf16", 0.0),
+    # the largest T whose bitmap fits the permutation's LDS for 128 experts
+    # (its rows keep the even word stride) and two batches of id loads
+    ("bf16_e128k8s1_t2560_lds_edge", 512, 256, 128, 8, 1, 2560, "bf16", 0.0),
 ]
 
 ROUTE_PERMUTE_BUFFERS = ("topk_ids", "topk_w", "expert_offsets", "row_token", "token_row", "sched", "x_q", "x_scale")
