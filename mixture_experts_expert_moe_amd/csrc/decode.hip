@@ -415,11 +415,15 @@ __global__ __launch_bounds__(kThreads) void decode_layer_kernel(DecodeArgs a) {
   }
   if ((E & 1) && tid < T) L.u.route.key[tid * kTopkKeys + E] = kNoKey;
   __syncthreads();
-  // top-k by rank counts: token t gets P = 8 / (the power of two >= T) waves
-  // (one wave per token from 8 tokens on), which split its keys; the counts
-  // meet in LDS (integer atomics: exact in any order), then one wave selects
-  {
-    const int P = T <= 1 ? 8 : T <= 2 ? 4 : T <= 4 ? 2 : 1;
+  // top-k: up to 4 tokens by rank counts, token t getting P = 8 / (the power
+  // of two >= T) waves, which split its keys; the counts meet in LDS
+  // (integer atomics: exact in any order), then one wave selects.  From 5
+  // tokens on a token has one wave: rounds of maxima (topk_wave_max).
+  if (T > 4) {
+    for (int t = wave; t < T; t += kWaves)
+      topk_wave_max_any(L.u.route.logit + t * E, E, k, L.ids + t * k, L.gate + t * k, nullptr, L.u.route.sel[wave]);
+  } else {
+    const int P = T <= 1 ? 8 : T <= 2 ? 4 : 2;  // T <= 4
     for (int tw = wave; tw < T * P; tw += kWaves) {
       const int t = tw / P, part = tw % P;
       const int chunk = ((E + P - 1) / P + 1) & ~1;

@@ -185,6 +185,69 @@ __device__ __forceinline__ void select_token(const float* logit, const int32_t* 
   topk_select<kPer>(val, above, E, k, ids, w, ids_copy, s_sel);
 }
 
+// Maximum of a 64-bit value over the wave (the pattern of wave_max_dpp on
+// both 32-bit halves); every lane of the wave must be active.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ long long dpp_max_i64(long long v) {
+  const int lo = (int)(v & 0xffffffffll), hi = (int)(v >> 32);
+  const int nlo = dpp_i32<kCtrl, kRowMask>(lo, lo), nhi = dpp_i32<kCtrl, kRowMask>(hi, hi);
+  const long long n = ((long long)nhi << 32) | (unsigned)nlo;
+  return n > v ? n : v;
+}
+__device__ __forceinline__ long long wave_max_i64(long long v) {
+  v = dpp_max_i64<kDppShr1, 0xf>(v);
+  v = dpp_max_i64<kDppShr2, 0xf>(v);
+  v = dpp_max_i64<kDppShr4, 0xf>(v);
+  v = dpp_max_i64<kDppShr8, 0xf>(v);
+  v = dpp_max_i64<kDppBcast15, 0xa>(v);
+  v = dpp_max_i64<kDppBcast31, 0xc>(v);
+  const int lo = __builtin_amdgcn_readlane((int)(v & 0xffffffffll), kWave - 1);
+  const int hi = __builtin_amdgcn_readlane((int)(v >> 32), kWave - 1);
+  return ((long long)hi << 32) | (unsigned)lo;
+}
+
+// Top-k of one token by one wave in k rounds of a wave-wide maximum over the
+// keys (all distinct), each taking out the largest key left: the candidate
+// taken in round r has rank r, so topk_select gets the same ranks as from
+// counting keys.  Used where a token has a wave to itself: counting ranks
+// then costs each lane E / 64 x E key comparisons, the rounds k reductions.
+// logit: the token's E logits (global or shared memory).
+template <int kPer>
+__device__ __forceinline__ void topk_wave_max(const float* logit, int E, int k, int32_t* ids, float* w,
+                                              int32_t* ids_copy, float* s_sel) {
+  const int lane = threadIdx.x % kWave;
+  long long key[kPer];
+  float val[kPer];
+  int above[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    val[j] = e < E ? logit[e] : 0.f;
+    key[j] = e < E ? topk_key(val[j], e) : kNoKey;
+    above[j] = k;
+  }
+  for (int r = 0; r < k; ++r) {
+    long long m = key[0];
+#pragma unroll
+    for (int j = 1; j < kPer; ++j) m = key[j] > m ? key[j] : m;
+    m = wave_max_i64(m);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (key[j] == m) {
+        above[j] = r;
+        key[j] = kNoKey;
+      }
+    }
+  }
+  topk_select<kPer>(val, above, E, k, ids, w, ids_copy, s_sel);
+}
+__device__ __forceinline__ void topk_wave_max_any(const float* logit, int E, int k, int32_t* ids, float* w,
+                                                  int32_t* ids_copy, float* s_sel) {
+  if (E <= kWave) topk_wave_max<1>(logit, E, k, ids, w, ids_copy, s_sel);
+  else if (E <= 2 * kWave) topk_wave_max<2>(logit, E, k, ids, w, ids_copy, s_sel);
+  else topk_wave_max<4>(logit, E, k, ids, w, ids_copy, s_sel);
+}
+
 // Row `row` of src by one block of NT threads: s = max|v| / 127 (IEEE
 // division), q = clamp(rne(v / s), -127, 127); s = 0 gives q = 0.  The block
 // may call this for several rows in turn.

@@ -62,7 +62,7 @@ __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(RoutePermute
   if (tok) {
     const int chunk = ((E + P - 1) / P + 1) & ~1;
     const int lo = part * chunk, hi = min(E, lo + chunk);
-    if (lo < hi) {
+    if (lo < hi && P > 1) {  // a token with one wave: ranked by topk_wave_max below
       const long long* keys = s_key + t * kTopkKeys;
       if (E <= kWave) rank_part<1>(keys, E, lo, hi, s_above + t * E);
       else if (E <= 2 * kWave) rank_part<2>(keys, E, lo, hi, s_above + t * E);
@@ -81,7 +81,8 @@ __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(RoutePermute
       const int32_t* ab = s_above + t * E;
       int32_t* ids = a.r.topk_ids + t * k;
       float* w = a.r.topk_w + t * k;
-      if (E <= kWave) select_token<1>(lg, ab, E, k, ids, w, s_ids + t * k, s_sel[t]);
+      if (P == 1) topk_wave_max_any(lg, E, k, ids, w, s_ids + t * k, s_sel[t]);
+      else if (E <= kWave) select_token<1>(lg, ab, E, k, ids, w, s_ids + t * k, s_sel[t]);
       else if (E <= 2 * kWave) select_token<2>(lg, ab, E, k, ids, w, s_ids + t * k, s_sel[t]);
       else select_token<4>(lg, ab, E, k, ids, w, s_ids + t * k, s_sel[t]);
     }
