@@ -210,7 +210,8 @@ __global__ __launch_bounds__(kWave* kRoute32Waves) void route_logits32_kernel(co
   }
 }
 
-// One wave per token: the rank-count top-k and gates of route_permute.hpp.
+// One wave per token: the top-k by rounds of wave-wide maxima and the gates
+// of route_permute.hpp.
 // kSlices > 0: the token's logits are first summed from kSlices fp64
 // partials in slice order, rounded once (+ bias), and written out.
 template <int kSlices>
@@ -220,7 +221,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                                                         float* __restrict__ logits_out,
                                                         int32_t* __restrict__ topk_ids,
                                                         float* __restrict__ topk_w, int T, int E, int k) {
-  __shared__ long long s_key[4][kTopkKeys];
   __shared__ float s_sel[4][16];
   __shared__ float s_row[kSlices > 0 ? 4 : 1][256];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
     wave_lds_sync();
     row = s_row[wave];
   }
-  topk_wave(row, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, nullptr, s_key[wave], s_sel[wave]);
+  topk_wave_max_any(row, E, k, topk_ids + (size_t)t * k, topk_w + (size_t)t * k, nullptr, s_sel[wave]);
 }
 
 }  // namespace

@@ -123,36 +123,6 @@ __device__ __forceinline__ void topk_select(const float (&val)[kPer], const int 
   if (lane < k) w[lane] = (float)(ex / den);
 }
 
-// Top-k of one token by one wave: each lane ranks its candidates against all
-// E keys, read back from LDS.  `row` holds the token's E logits (global or
-// shared memory); s_key: kTopkKeys keys of LDS scratch for this wave.
-template <int kPer>
-__device__ __forceinline__ void topk_wave_t(const float* row, int E, int k, int32_t* ids, float* w,
-                                            int32_t* ids_copy, long long* s_key, float* s_sel) {
-  const int lane = threadIdx.x % kWave;
-  long long key[kPer];
-  float val[kPer];
-  int above[kPer];
-#pragma unroll
-  for (int j = 0; j < kPer; ++j) {
-    const int e = lane + kWave * j;
-    val[j] = e < E ? row[e] : 0.f;
-    key[j] = e < E ? topk_key(val[j], e) : kNoKey;
-    if (e < E) s_key[e] = key[j];
-    above[j] = 0;
-  }
-  if (lane == 0 && (E & 1)) s_key[E] = kNoKey;
-  wave_lds_sync();
-  topk_count<kPer>(s_key, 0, E, key, above);
-  topk_select<kPer>(val, above, E, k, ids, w, ids_copy, s_sel);
-}
-__device__ __forceinline__ void topk_wave(const float* row, int E, int k, int32_t* ids, float* w, int32_t* ids_copy,
-                                          long long* s_key, float* s_sel) {
-  if (E <= kWave) topk_wave_t<1>(row, E, k, ids, w, ids_copy, s_key, s_sel);
-  else if (E <= 2 * kWave) topk_wave_t<2>(row, E, k, ids, w, ids_copy, s_key, s_sel);
-  else topk_wave_t<4>(row, E, k, ids, w, ids_copy, s_key, s_sel);
-}
-
 // Ranks of token t's candidates against the keys of one part of its E.
 template <int kPer>
 __device__ __forceinline__ void rank_part(const long long* keys, int E, int lo, int hi, int32_t* above_sum) {
