@@ -5,9 +5,10 @@
 // the sum of the partials in slice order rounded once to fp32 (+ bias), the
 // top-k and gates of every token, the permutation with its tile schedule,
 // and, for int8 weights, the per-token quantisation of x.  The top-k keys,
-// rank counts, selection and gates, the int8 code and the permutation are
-// the same device functions the stand-alone kernels call, so the results
-// agree bit for bit.  Few-token calls are decode steps, where the pages find
+// the selection and gates, the int8 code and the permutation are the same
+// device functions the stand-alone kernels call, and the ranks are the same
+// whether counted or taken by rounds of maxima, so the results agree bit for
+// bit.  Few-token calls are decode steps, where the pages find
 // the launch count, not the arithmetic, to be the cost ("MoE Decode
 // Partition and Submit Floor", section 3; "~2.7s fixed per-request TTFT ...
 // concatenated-expert GEMM", section "Evidence").
@@ -25,7 +26,8 @@ static_assert(kSmallRouteT <= kFewTokens, "few-token permutation");
 // they split the key range of its top-k ranks (partial counts summed with
 // LDS atomics, exact in any order) and the columns of its int8 quantisation
 // (slice maxima combined after a barrier).  Wave part 0 then selects the k
-// experts and their gates.
+// experts and their gates.  With one wave per token (from 9 tokens on) that
+// wave takes the ranks by rounds of maxima (topk_wave_max) instead.
 template <bool kF32>
 __global__ __launch_bounds__(kPermThreads) void route_finish_kernel(RoutePermuteArgs a) {
   __shared__ float s_logit[kSmallRouteT * 256];             // T x E logits
