@@ -75,8 +75,8 @@ static_assert(MOE_BIG_RING_MX >= 3 && MOE_BIG_RING_MX <= 4, "ring depth");
 static_assert(MOE_BIG_RING_SHORT >= 2 && MOE_BIG_RING_SHORT <= 4, "ring depth");
 // Waves per block: 4-bit eight (two per SIMD; the 4-bit decode is VALU-bound,
 // and one wave per SIMD issues VALU instructions at well under the SIMD's
-// rate), the other formats four.  Each wave owns 256 / (16 waves) weight
-// fragments of 16 rows.
+// rate), the other formats four.  Each wave owns 256 / (16 x waves)
+// fragments of 16 weight rows.
 template <int WF> constexpr int big_waves() { return WF == kQ4 ? 8 : 4; }
 template <int WF> constexpr int big_threads() { return kWave * big_waves<WF>(); }
 template <int WF> constexpr int frags() { return kBN / 16 / big_waves<WF>(); }
