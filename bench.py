@@ -187,6 +187,28 @@ class Runner:
                    for j, n in enumerate(names)}
         return wall, U, kms
 
+    def graph_timed(self, replays):
+        """Wall time per step of the same layer steps captured in one HIP graph
+        (one step per weight set, each on its own token batch) and replayed:
+        the layer without the host's launch gaps."""
+        torch = self.torch
+        n = len(self.wsets)
+        for i in range(n):
+            self.step(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                self.step(i)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(replays):
+            g.replay()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / (replays * n)
+
 
 def cpu_model():
     try:
@@ -451,6 +473,9 @@ def main():
                                          / MFMA_BF16_PEAK_TFLOPS, 4),
             "layer_hbm_frac": round((gu_bytes + dn_bytes) / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
         })
+        # the same steps replayed from a captured HIP graph (no host launch gaps)
+        g_s = r.graph_timed(max(1, args.steps // len(r.wsets)))
+        extra["graph_replay"] = {"tokens_per_s": round(T / g_s, 1), "ms_per_step": round(g_s * 1e3, 5)}
         del r
         torch.cuda.empty_cache()
 
