@@ -303,6 +303,12 @@ FUSED_ROUTE = [
     # one token without a shared expert: k = 16 of 256, and k = E
     ("bf16_e256k16_t1", 1024, 256, 256, 16, 0, 1, "bf16", 0.0),
     ("bf16_e8k8_t1", 256, 256, 8, 8, 0, 1, "bf16", 0.0),
+    # an expert count that is not a multiple of 64 (padding keys in the rounds
+    # of maxima): one wave per token in the fused block (T = 9), and T > 16
+    ("bf16_e100k6s1_t9", 256, 256, 100, 6, 1, 9, "bf16", 0.0),
+    ("bf16_e100k6s1_t40", 256, 256, 100, 6, 1, 40, "bf16", 0.0),
+    # 32 x 32 router blocks over 256 experts (eight expert blocks)
+    ("bf16_e256k16_t1024", 512, 256, 256, 16, 0, 1024, "bf16", 0.0),
     # the largest T whose bitmap fits the permutation's LDS for 128 experts
     # (its rows keep the even word stride) and two batches of id loads
     ("bf16_e128k8s1_t2560_lds_edge", 512, 256, 128, 8, 1, 2560, "bf16", 0.0),
